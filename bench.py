@@ -1,0 +1,215 @@
+"""Throughput of the MoE expert layer on one MI355X.
+
+python bench.py [--gpus 1] [--steps K] [--warmup W] [--config NAME] [--layers L]
+
+A step is one moe_layer call (router + top-k, permute, grouped SwiGLU FFN,
+shared expert, combine) over one batch of T tokens. Steps cycle through L
+independently generated layers (as consecutive MoE layers of a model would),
+so the weights of the step being timed are not still sitting in the 256 MB
+last-level cache from the step before; L is chosen so the L layers' weights
+exceed 1 GB. Inputs are resident in HBM before the timed region.
+
+Prints one JSON line: value = tokens/s over the K timed steps, plus the
+roofline of the dominant kernel (the routed experts' gate/up projection with
+SwiGLU: algorithmic bytes per launch / its mean duration from HIP events
+recorded on the layer's stream around every launch) and the CPU oracle's
+throughput on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0      # dense bf16 matrix cores
+INT8_PEAK_TOPS = 5000.0        # dense int8 matrix cores
+FP32_PEAK_TFLOPS = 157.3
+DEFAULT_CONFIG = "longcat_zero_bf16"
+METRIC = "MoE-layer tokens/s at 1 GPU; decode HBM GB/s %peak; prefill MFMA %peak"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "ffn1_traffic.json")
+KERNEL_SRC = os.path.join(ROOT, "moe_expert_layer_fp32_amd", "csrc", "gemm.hip")
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--config", default=DEFAULT_CONFIG)
+    p.add_argument("--layers", type=int, default=0, help="layers cycled (0: enough for > 1 GB of weights)")
+    p.add_argument("--cpu-seconds", type=float, default=10.0, help="target CPU time of the oracle sample")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    return p.parse_args()
+
+
+def kernel_hash() -> str:
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def ffn1_algorithmic(cfg, counts_per_layer):
+    """Algorithmic work of one launch of the routed gate/up projection:
+    bytes = W1 and W3 of every resident expert that received tokens, the R
+    gathered activation rows (d elements each) and the R rows of h written
+    (I elements each); flops = 2 * R * d * 2I."""
+    wb = {"f32": 4, "bf16": 2, "w8a8": 1}[cfg.dtype]
+    xb = {"f32": 4, "bf16": 2, "w8a8": 1}[cfg.dtype]
+    hb = {"f32": 4, "bf16": 2, "w8a8": 4}[cfg.dtype]
+    out = []
+    for counts in counts_per_layer:
+        res = counts[cfg.ffn_begin:cfg.ffn_begin + cfg.n_ffn]
+        active = int((res > 0).sum())
+        R = int(res.sum())
+        wbytes = active * 2 * cfg.d * cfg.inter * wb
+        if cfg.dtype == "w8a8":
+            wbytes += active * 2 * cfg.inter * 4        # fp32 column scales
+        byts = wbytes + R * cfg.d * xb + R * cfg.inter * hb
+        flops = 2.0 * R * cfg.d * 2 * cfg.inter
+        out.append((byts, flops, R, active))
+    return out
+
+
+def cpu_baseline(cfg, inp, seconds: float):
+    """The oracle as it stands, timed on this host on a bounded sample."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    from oracle import moe_oracle as O
+
+    sample = cfg.T
+    if cfg.T * cfg.d * max(cfg.inter, cfg.shared_inter, 1) > 256 * 1024 * 2048:
+        sample = 64
+    toks = np.arange(sample)
+    t0 = time.perf_counter()
+    n = 0
+    while True:
+        O.moe_layer(inp, cfg, tokens=toks)
+        n += sample
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    return {"value": n / el, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{n} tokens: {n // sample} oracle calls on the first {sample} tokens of the "
+                      f"{cfg.name} batch, {el:.1f} s wall, numpy fp64 with {threads} BLAS threads"}
+
+
+def main() -> int:
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the MoE layer here is one device's share and this "
+              "build has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    from moe_expert_layer_fp32_amd import lib as L
+    from moe_expert_layer_fp32_amd.layer import DeviceLayer
+    from moe_inputs import get, make_inputs
+
+    cfg = get(args.config)
+    per_layer_bytes = max(1, (cfg.n_ffn * 3 * cfg.d * cfg.inter + 3 * cfg.d * cfg.shared_inter)
+                          * {"f32": 4, "bf16": 2, "w8a8": 1}[cfg.dtype])
+    n_layers = args.layers or max(1, min(8, -(-(1 << 30) // per_layer_bytes)))
+    torch.cuda.set_device(0)
+    layers, inputs0 = [], None
+    for s in range(n_layers):
+        inp = make_inputs(cfg, seed=cfg.seed + s)
+        if s == 0:
+            inputs0 = inp
+        layers.append(DeviceLayer(cfg, inp))
+        if s:
+            del inp
+    desc = layers[0].desc
+    ws = layers[0].workspace(L.OP_LAYER)
+    y = torch.empty((cfg.T, cfg.d), dtype=layers[0].xdtype, device="cuda")
+
+    # Routing tables of each layer (outside the timed region) for the
+    # algorithmic byte count of the dominant kernel.
+    counts_per_layer = []
+    for lay in layers:
+        _, t = lay.layer_with_tables()
+        counts_per_layer.append(t["counts"].cpu().numpy())
+    torch.cuda.synchronize()
+
+    K, W = args.steps, args.warmup
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    for a, b in ev:               # create the underlying HIP events
+        a.record()
+        b.record()
+    torch.cuda.synchronize()
+    auxes = [L.MoeAux(ev_ffn1_begin=a.cuda_event, ev_ffn1_end=b.cuda_event) for a, b in ev]
+
+    for i in range(W):
+        lay = layers[i % n_layers]
+        L.moe_layer(desc, lay.weights, lay.x, y, None, ws)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        lay = layers[i % n_layers]
+        L.moe_layer(desc, lay.weights, lay.x, y, auxes[i], ws)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    ffn1_ms = np.array([a.elapsed_time(b) for a, b in ev])
+    alg = ffn1_algorithmic(cfg, counts_per_layer)
+    alg_bytes = np.array([alg[i % n_layers][0] for i in range(K)])
+    alg_flops = np.array([alg[i % n_layers][1] for i in range(K)])
+    mean_s = float(ffn1_ms.mean()) / 1e3
+    prefill = cfg.T >= 4096
+    if prefill:
+        peak = INT8_PEAK_TOPS if cfg.dtype == "w8a8" else (FP32_PEAK_TFLOPS if cfg.dtype == "f32" else BF16_PEAK_TFLOPS)
+        achieved = float(alg_flops.mean()) / mean_s / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s"}
+    else:
+        achieved = float(alg_bytes.mean()) / mean_s / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s"}
+    roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
+    roof["kernel"] = "gemm_rows_kernel (routed gate/up + SwiGLU)"
+    roof["mean_us"] = round(mean_s * 1e6, 2)
+    roof["alg_bytes_per_launch"] = int(alg_bytes.mean())
+    roof["traffic"] = None
+    if os.path.exists(TRAFFIC_FILE):
+        tr = json.load(open(TRAFFIC_FILE))
+        if tr.get("kernel_sha") == kernel_hash() and tr.get("workload") == cfg.name:
+            roof["traffic"] = tr.get("bytes_per_launch")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(cfg, inputs0, args.cpu_seconds)
+
+    rec = {
+        "metric": METRIC,
+        "value": round(cfg.T * K / wall, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": round(wall / K * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": {"f32": "f32", "bf16": "bf16", "w8a8": "int8"}[cfg.dtype],
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "T": cfg.T, "d": cfg.d, "E": cfg.E, "k": cfg.k, "gate": cfg.gate,
+                   "n_ffn": cfg.n_ffn, "n_zero": cfg.n_zero, "inter": cfg.inter,
+                   "shared_inter": cfg.shared_inter, "layers_cycled": n_layers,
+                   "global_batch": cfg.T, "parallelism": "none (1 GPU)"},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,262 @@
+/*
+ * moe.h - C ABI of libmoe.so, the MI355X (gfx950) MoE expert layer.
+ *
+ * One MoE expert layer of a sparse LLM on one device: router matmul and top-k
+ * gating, the reordering of tokens by expert, grouped SwiGLU FFN over the
+ * resident experts (weight streaming when an expert has few tokens, MFMA
+ * tiles when it has many), zero-computation identity experts, the shared
+ * expert, and the weighted combine back into token order.
+ *
+ * Sources, cited by page title and section (the pages give no formula; the
+ * readings taken where they are silent are listed with the oracle):
+ *  - Router Matmul, QuantBatchMatmul: page "基于Atlas 900 A3 SuperPoD的
+ *    LongCat-Flash模型推理性能优化实践", section 优化措施三 (权重预取).
+ *  - Zero-computation experts: same page, section 背景介绍; and page
+ *    "LongCat-Flash与GLM-4.6V ...", section 拆解MoE困局.
+ *  - Grouped experts (MoGE), SwiftGMM's GEMV/GEMM switch by per-expert load:
+ *    page "华为技术披露集 VOL.12：昇腾×盘古", opening section and section
+ *    SwiftGMM.
+ *  - InitialRouting (sort all tokens by expert) and Dispatch/Combine: page on
+ *    DeepSeek-V3/R1 on Ascend (Huxiu), section MOE 算子优化.
+ *  - One card's share: 8 routed + 1 shared expert per card, same page,
+ *    opening section.
+ *
+ * Conventions for every entry point
+ *  - Every tensor pointer is DEVICE memory owned by the caller. The library
+ *    never allocates, frees or keeps anything between calls; scratch memory
+ *    is the caller's workspace (size from moe_workspace_bytes).
+ *  - `stream` is a hipStream_t (NULL = the null stream). All work is enqueued
+ *    on it; no entry point synchronises the host or copies device data to
+ *    the host, so calls are legal under stream capture.
+ *  - Arguments are validated on the host before anything is enqueued; on
+ *    error a negative status is returned and nothing was launched.
+ *  - Row-major layouts throughout. bf16 is the 16-bit brain float (upper
+ *    half of an fp32). Results are deterministic: the same inputs give
+ *    bit-identical outputs (no floating-point atomics).
+ *  - Preconditions not checked on the device: inputs are finite.
+ */
+#ifndef MOE_H_
+#define MOE_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t moe_status;
+#define MOE_OK 0
+#define MOE_ERR_INVALID_ARG (-1) /* null pointer, inconsistent sizes, bad ids */
+#define MOE_ERR_UNSUPPORTED (-2) /* shape or option outside what is built */
+#define MOE_ERR_WORKSPACE (-3)   /* workspace smaller than moe_workspace_bytes */
+#define MOE_ERR_HIP (-4)         /* a HIP call or launch failed */
+
+/* gate */
+#define MOE_GATE_SOFTMAX 0 /* scores = softmax over the E logits */
+#define MOE_GATE_SIGMOID 1 /* scores = logistic sigmoid of each logit */
+
+/* arithmetic type of the layer */
+#define MOE_DTYPE_F32 0  /* x, expert weights, y fp32 */
+#define MOE_DTYPE_BF16 1 /* x, expert weights, y bf16; fp32 accumulation */
+#define MOE_DTYPE_W8A8 2 /* x, y bf16; int8 weights with fp32 per-output-
+                            channel scales; activations quantised to int8 per
+                            row inside the layer; int32 accumulation */
+
+/* which FFN moe_grouped_ffn computes */
+#define MOE_FFN_ROUTED 0
+#define MOE_FFN_SHARED 1
+
+/* weight parts for moe_packed_bytes / moe_pack_weights */
+#define MOE_PACK_ROUTER 0 /* src_a = W_r [d][E] fp32                         */
+#define MOE_PACK_W13 1    /* src_a = W1, src_b = W3: [n_ffn][d][I]           */
+#define MOE_PACK_W2 2     /* src_a = W2: [n_ffn][I][d]                       */
+#define MOE_PACK_SW13 3   /* src_a = shared W1, src_b = shared W3: [d][I_s]  */
+#define MOE_PACK_SW2 4    /* src_a = shared W2: [I_s][d]                     */
+
+/* ops for moe_workspace_bytes */
+#define MOE_OP_ROUTE_TOPK 0
+#define MOE_OP_PERMUTE 1
+#define MOE_OP_FFN_ROUTED 2
+#define MOE_OP_FFN_SHARED 3
+#define MOE_OP_COMBINE 4
+#define MOE_OP_LAYER 5
+
+/*
+ * Layer descriptor (host memory, read during the call only).
+ *
+ * Selection rules (exactly one applies):
+ *  - plain: n_group == 1 (or topk_group == 0 and per_group_k == 0): the k
+ *    largest scores;
+ *  - group-limited: topk_group > 0: experts form n_group contiguous groups of
+ *    E/n_group; a group scores the sum of its two largest expert scores; the
+ *    topk_group best groups are kept and the k largest scores among their
+ *    experts are chosen;
+ *  - per-group quota (MoGE): per_group_k > 0: the per_group_k largest of
+ *    every group; k must equal n_group * per_group_k.
+ * Selections of a token are ordered by descending score; equal scores go to
+ * the lower expert (or group) index. A logit bias, when given, is added to
+ * the logits before the gate, so it moves both selection and weights.
+ * Weights: the selected scores, divided by their sum when renorm != 0, times
+ * route_scale.
+ *
+ * Expert ids [ffn_begin, ffn_begin + n_ffn) are SwiGLU FFN experts resident
+ * on this device; [zero_begin, zero_begin + n_zero) are identity experts
+ * (output = input); any other id is an expert held elsewhere and contributes
+ * nothing here. The two ranges must not overlap.
+ *
+ * Limits: 1 <= E <= 256; 1 <= k <= min(E, 16); d, inter, shared_inter
+ * multiples of 64; T * k <= 2^20; E divisible by n_group; group-limited
+ * needs E/n_group >= 2.
+ */
+typedef struct moe_desc {
+    int32_t T;            /* tokens (0 is allowed: every call is a no-op) */
+    int32_t d;            /* hidden size */
+    int32_t E;            /* experts scored by the router */
+    int32_t k;            /* experts selected per token */
+    int32_t gate;         /* MOE_GATE_* */
+    int32_t n_group;      /* contiguous expert groups (1 = none) */
+    int32_t topk_group;   /* group-limited routing: groups kept (0 = off) */
+    int32_t per_group_k;  /* MoGE: experts taken from every group (0 = off) */
+    int32_t renorm;       /* != 0: divide weights by their sum */
+    float route_scale;    /* multiplies every weight */
+    int32_t ffn_begin;    /* first resident FFN expert id */
+    int32_t n_ffn;        /* resident FFN experts */
+    int32_t zero_begin;   /* first identity expert id */
+    int32_t n_zero;       /* identity experts */
+    int32_t inter;        /* FFN inner size I of the routed experts */
+    int32_t shared_inter; /* inner size of the shared expert (0 = none) */
+    int32_t dtype;        /* MOE_DTYPE_* */
+} moe_desc;
+
+/*
+ * Weights (device pointers). Expert and router weights are consumed in the
+ * packed layout written by moe_pack_weights (a one-time conversion of the
+ * logical x*W layouts; the packed form is private to the library and its
+ * size is moe_packed_bytes). Unused members may be NULL.
+ */
+typedef struct moe_weights {
+    const void* router;     /* packed MOE_PACK_ROUTER */
+    const float* logit_bias;/* [E] fp32, or NULL */
+    const void* w13;        /* packed MOE_PACK_W13 (n_ffn > 0) */
+    const void* w2;         /* packed MOE_PACK_W2  (n_ffn > 0) */
+    const float* s1;        /* W8A8: [n_ffn][I] scale of W1 columns */
+    const float* s3;        /* W8A8: [n_ffn][I] scale of W3 columns */
+    const float* s2;        /* W8A8: [n_ffn][d] scale of W2 columns */
+    const void* sw13;       /* packed MOE_PACK_SW13 (shared_inter > 0) */
+    const void* sw2;        /* packed MOE_PACK_SW2  (shared_inter > 0) */
+    const float* ss1;       /* W8A8: [I_s] */
+    const float* ss3;       /* W8A8: [I_s] */
+    const float* ss2;       /* W8A8: [d]   */
+} moe_weights;
+
+/*
+ * Optional outputs and hooks of moe_layer; any NULL member is skipped. The
+ * table members, when given, are written instead of workspace copies (same
+ * contents as moe_route_topk / moe_permute produce). The events (hipEvent_t)
+ * are recorded on `stream` around the stages of the layer, for timing.
+ */
+typedef struct moe_aux {
+    int32_t* topk_idx;    /* [T][k] */
+    float* topk_w;        /* [T][k] */
+    int32_t* counts;      /* [E] */
+    int32_t* offsets;     /* [E+1] */
+    int32_t* sorted_slot; /* [T*k] */
+    int32_t* slot_pos;    /* [T*k] */
+    int8_t* q_x;          /* W8A8: [T][d] per-token int8 codes of x */
+    float* s_x;           /* W8A8: [T] their scales */
+    void* ev_ffn1_begin;  /* recorded before / after the routed-expert       */
+    void* ev_ffn1_end;    /*   gate/up projection + SwiGLU kernel            */
+    void* ev_ffn2_begin;  /* recorded before / after the routed-expert down  */
+    void* ev_ffn2_end;    /*   projection kernel                             */
+} moe_aux;
+
+/* Workspace bytes an entry point needs for this descriptor (0 if none). */
+size_t moe_workspace_bytes(const moe_desc* desc, int op);
+
+/* Human-readable name of a status code (static storage). */
+const char* moe_status_str(moe_status status);
+
+/* Bytes of the packed form of one weight part (MOE_PACK_*). */
+size_t moe_packed_bytes(const moe_desc* desc, int part);
+
+/*
+ * Convert one weight part from its logical layout into the packed layout the
+ * kernels stream (fragment-major tiles of 16 output columns, each fragment
+ * laid out as one matrix-core operand, so a wavefront reads 1 KiB of
+ * contiguous memory per load). For MOE_PACK_ROUTER with a bf16 or W8A8
+ * layer, W_r is stored as three bf16 planes hi + mid + lo whose sum is
+ * exactly W_r (a bf16 activation times each plane is exact in fp32, so the
+ * router stays an fp32-accurate product on bf16 matrix cores).
+ * src_a / src_b: logical weights in the layer's weight type (fp32, bf16, or
+ * int8 for W8A8 experts; the router is always fp32). dst: dst_bytes >=
+ * moe_packed_bytes. Enqueued on `stream`.
+ */
+moe_status moe_pack_weights(const moe_desc* desc, int part, const void* src_a,
+                            const void* src_b, void* dst, size_t dst_bytes,
+                            void* stream);
+
+/*
+ * Router matmul + gating + top-k.
+ * x: [T][d] (fp32 for MOE_DTYPE_F32, else bf16).
+ * Out: topk_idx [T][k] int32 expert ids; topk_w [T][k] fp32 gate weights.
+ */
+moe_status moe_route_topk(const moe_desc* desc, const moe_weights* w,
+                          const void* x, int32_t* topk_idx, float* topk_w,
+                          void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Stable counting sort of the T*k slots (slot s = t*k + j) by expert id.
+ * Out: counts [E] (slots per expert), offsets [E+1] (exclusive prefix sum),
+ * sorted_slot [T*k] (slots in ascending (expert, s) order), slot_pos [T*k]
+ * (inverse: sorted_slot[slot_pos[s]] == s). An id outside [0, E) is dropped:
+ * it is not counted and its slot_pos is -1. Bit-exact and deterministic.
+ */
+moe_status moe_permute(const moe_desc* desc, const int32_t* topk_idx,
+                       int32_t* counts, int32_t* offsets, int32_t* sorted_slot,
+                       int32_t* slot_pos, void* ws, size_t ws_bytes,
+                       void* stream);
+
+/*
+ * Grouped SwiGLU FFN. MOE_FFN_ROUTED: for each resident expert e and each
+ * sorted row r in [offsets[e], offsets[e+1]), token t = sorted_slot[r] / k,
+ * rows[r - offsets[ffn_begin]] = W2_e^T (silu(x_t W1_e) * (x_t W3_e)).
+ * Rows with fewer tokens are streamed weight-first (each weight byte read
+ * once); experts with many tokens run as MFMA tiles; the choice is made on
+ * the device from the offsets. MOE_FFN_SHARED: the shared expert for every
+ * token, rows[t] (offsets, sorted_slot ignored).
+ * x: [T][d] (fp32 or bf16 by dtype; W8A8 quantises it per token inside).
+ * rows: fp32, capacity T*k rows (routed) or T rows (shared), d columns.
+ */
+moe_status moe_grouped_ffn(const moe_desc* desc, const moe_weights* w,
+                           int which, const void* x, const int32_t* offsets,
+                           const int32_t* sorted_slot, float* rows, void* ws,
+                           size_t ws_bytes, void* stream);
+
+/*
+ * Weighted combine back into token order:
+ * y[t] = shared_rows[t] + sum_j topk_w[t][j] * u_tj, where u_tj is
+ * rows[slot_pos[t*k+j] - offsets[ffn_begin]] for a resident FFN expert,
+ * x[t] for an identity expert and 0 otherwise; fp32 sums in slot order,
+ * rounded once to y's type (fp32 for MOE_DTYPE_F32, else bf16).
+ * shared_rows may be NULL (no shared expert).
+ */
+moe_status moe_combine(const moe_desc* desc, const void* x, const float* rows,
+                       const float* shared_rows, const int32_t* topk_idx,
+                       const float* topk_w, const int32_t* offsets,
+                       const int32_t* slot_pos, void* y, void* stream);
+
+/*
+ * The whole layer: route_topk -> permute -> (W8A8: quantise x) -> routed
+ * FFN -> shared FFN -> combine, in one call. x: [T][d]; y: [T][d] (types as
+ * in moe_combine). aux may be NULL.
+ */
+moe_status moe_layer(const moe_desc* desc, const moe_weights* w, const void* x,
+                     void* y, moe_aux* aux, void* ws, size_t ws_bytes,
+                     void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_H_ */

@@ -1,0 +1,497 @@
+// C ABI of libmoe.so: argument validation, workspace layout and the order of
+// kernel launches for each entry point (declared and documented in moe.h).
+// Nothing here allocates, synchronises or copies to the host; every launch
+// goes on the caller's stream.
+#include <hip/hip_runtime_api.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdint>
+
+#include "kernels.h"
+#include "moe.h"
+
+using namespace moe;
+
+namespace {
+
+constexpr size_t ALIGN = 256;
+constexpr int MAX_E = 256;
+constexpr int MAX_K = 16;
+constexpr int64_t MAX_SLOTS = int64_t(1) << 20;
+
+size_t align_up(size_t v) { return (v + ALIGN - 1) / ALIGN * ALIGN; }
+int ceil_div(int a, int b) { return (a + b - 1) / b; }
+
+int e_pad(const moe_desc* d) { return (d->E + 15) / 16 * 16; }
+int x_bytes(const moe_desc* d) { return d->dtype == MOE_DTYPE_F32 ? 4 : 2; }
+int w_bytes(const moe_desc* d) { return d->dtype == MOE_DTYPE_F32 ? 4 : (d->dtype == MOE_DTYPE_BF16 ? 2 : 1); }
+// Element size of the SwiGLU output h kept between the two projections:
+// bf16 for the bf16 layer (the down projection consumes bf16 operands), fp32
+// otherwise (fp32 layer; W8A8 requantises it per row).
+int h_bytes(const moe_desc* d) { return d->dtype == MOE_DTYPE_BF16 ? 2 : 4; }
+bool w8a8(const moe_desc* d) { return d->dtype == MOE_DTYPE_W8A8; }
+// Capacity for routed rows on resident experts: T*k, the most the routing
+// tables can hold whatever ids they carry.
+int r_max(const moe_desc* d) { return d->n_ffn > 0 ? d->T * d->k : 0; }
+
+GemmElem weight_elem(const moe_desc* d) {
+  return d->dtype == MOE_DTYPE_F32 ? ELEM_F32 : (d->dtype == MOE_DTYPE_BF16 ? ELEM_BF16 : ELEM_I8);
+}
+int weight_kf(const moe_desc* d) { return d->dtype == MOE_DTYPE_F32 ? 4 : (d->dtype == MOE_DTYPE_BF16 ? 32 : 64); }
+int frag_bytes_of(GemmElem e) { return e == ELEM_F32 ? 64 * 4 : 64 * 16; }
+
+moe_status validate(const moe_desc* d) {
+  if (!d) return MOE_ERR_INVALID_ARG;
+  if (d->T < 0 || d->d <= 0 || d->E < 1 || d->k < 1 || d->k > d->E) return MOE_ERR_INVALID_ARG;
+  if (d->gate != MOE_GATE_SOFTMAX && d->gate != MOE_GATE_SIGMOID) return MOE_ERR_INVALID_ARG;
+  if (d->dtype != MOE_DTYPE_F32 && d->dtype != MOE_DTYPE_BF16 && d->dtype != MOE_DTYPE_W8A8)
+    return MOE_ERR_INVALID_ARG;
+  if (d->n_group < 1 || d->E % d->n_group != 0) return MOE_ERR_INVALID_ARG;
+  if (d->topk_group < 0 || d->per_group_k < 0) return MOE_ERR_INVALID_ARG;
+  if (d->topk_group > 0 && d->per_group_k > 0) return MOE_ERR_INVALID_ARG;
+  const int gsize = d->E / d->n_group;
+  if (d->topk_group > 0) {
+    if (d->topk_group > d->n_group || gsize < 2 || d->k > d->topk_group * gsize) return MOE_ERR_INVALID_ARG;
+  }
+  if (d->per_group_k > 0) {
+    if (d->k != d->n_group * d->per_group_k || d->per_group_k > gsize) return MOE_ERR_INVALID_ARG;
+  }
+  if (d->ffn_begin < 0 || d->n_ffn < 0 || d->ffn_begin + d->n_ffn > d->E) return MOE_ERR_INVALID_ARG;
+  if (d->zero_begin < 0 || d->n_zero < 0 || d->zero_begin + d->n_zero > d->E) return MOE_ERR_INVALID_ARG;
+  if (d->n_ffn > 0 && d->n_zero > 0 && d->ffn_begin < d->zero_begin + d->n_zero &&
+      d->zero_begin < d->ffn_begin + d->n_ffn)
+    return MOE_ERR_INVALID_ARG;
+  if (d->n_ffn > 0 && d->inter <= 0) return MOE_ERR_INVALID_ARG;
+  if (d->shared_inter < 0 || d->inter < 0) return MOE_ERR_INVALID_ARG;
+  if (!std::isfinite(d->route_scale)) return MOE_ERR_INVALID_ARG;
+  // Built shapes.
+  if (d->E > MAX_E || d->k > MAX_K) return MOE_ERR_UNSUPPORTED;
+  if (int64_t(d->T) * d->k > MAX_SLOTS) return MOE_ERR_UNSUPPORTED;
+  if (d->d % 64 != 0 || d->inter % 64 != 0 || d->shared_inter % 64 != 0) return MOE_ERR_UNSUPPORTED;
+  if (d->topk_group > 0 && d->n_group > 64) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+// ---------------------------------------------------------------------------
+// workspace layouts
+// ---------------------------------------------------------------------------
+struct Carve {
+  uint8_t* base;
+  size_t used = 0;
+  explicit Carve(void* b) : base(static_cast<uint8_t*>(b)) {}
+  void* take(size_t bytes) {
+    void* p = base ? base + used : nullptr;
+    used += align_up(bytes);
+    return p;
+  }
+};
+
+struct RouteWs { float* z; };
+RouteWs carve_route(Carve& c, const moe_desc* d) {
+  return {static_cast<float*>(c.take(size_t(d->T) * e_pad(d) * 4))};
+}
+
+struct FfnWs {
+  int8_t* qx; float* sx;      // W8A8 activation codes (shared by routed and shared FFN)
+  uint8_t* h; int8_t* qh; float* sh;
+};
+void carve_qx(Carve& c, const moe_desc* d, FfnWs& f) {
+  f.qx = nullptr; f.sx = nullptr;
+  if (w8a8(d)) {
+    f.qx = static_cast<int8_t*>(c.take(size_t(d->T) * d->d));
+    f.sx = static_cast<float*>(c.take(size_t(d->T) * 4));
+  }
+}
+void carve_h(Carve& c, const moe_desc* d, int rows, int inter, FfnWs& f) {
+  f.h = static_cast<uint8_t*>(c.take(size_t(rows) * inter * h_bytes(d)));
+  f.qh = nullptr; f.sh = nullptr;
+  if (w8a8(d)) {
+    f.qh = static_cast<int8_t*>(c.take(size_t(rows) * inter));
+    f.sh = static_cast<float*>(c.take(size_t(rows) * 4));
+  }
+}
+
+struct LayerWs {
+  RouteWs route;
+  int32_t *idx, *counts, *offsets, *sorted_slot, *slot_pos;
+  float* w;
+  FfnWs routed, shared;
+  float *rows, *shared_rows;
+};
+LayerWs carve_layer(Carve& c, const moe_desc* d) {
+  LayerWs L{};
+  const size_t slots = size_t(d->T) * d->k;
+  L.route = carve_route(c, d);
+  L.idx = static_cast<int32_t*>(c.take(slots * 4));
+  L.w = static_cast<float*>(c.take(slots * 4));
+  L.counts = static_cast<int32_t*>(c.take(size_t(d->E) * 4));
+  L.offsets = static_cast<int32_t*>(c.take(size_t(d->E + 1) * 4));
+  L.sorted_slot = static_cast<int32_t*>(c.take(slots * 4));
+  L.slot_pos = static_cast<int32_t*>(c.take(slots * 4));
+  carve_qx(c, d, L.routed);
+  L.shared.qx = L.routed.qx;
+  L.shared.sx = L.routed.sx;
+  carve_h(c, d, r_max(d), d->inter, L.routed);
+  L.rows = static_cast<float*>(c.take(size_t(r_max(d)) * d->d * 4));
+  if (d->shared_inter > 0) {
+    carve_h(c, d, d->T, d->shared_inter, L.shared);
+    L.shared_rows = static_cast<float*>(c.take(size_t(d->T) * d->d * 4));
+  } else {
+    L.shared_rows = nullptr;
+  }
+  return L;
+}
+
+// ---------------------------------------------------------------------------
+// stages
+// ---------------------------------------------------------------------------
+#define HIP_TRY(expr)                                    \
+  do {                                                   \
+    if ((expr) != hipSuccess) return MOE_ERR_HIP;        \
+  } while (0)
+
+moe_status run_route(const moe_desc* d, const moe_weights* w, const void* x, int32_t* idx, float* tw,
+                     const RouteWs& ws, hipStream_t s) {
+  GemmArgs g{};
+  const bool f32 = d->dtype == MOE_DTYPE_F32;
+  g.A = static_cast<const uint8_t*>(w->router);
+  g.a_group_stride = 0;
+  g.K = d->d;
+  g.N = e_pad(d);
+  g.B = static_cast<const uint8_t*>(x);
+  g.ldb = size_t(d->d) * x_bytes(d);
+  g.dense_rows = d->T;
+  g.out = reinterpret_cast<uint8_t*>(ws.z);
+  g.ldo = size_t(e_pad(d)) * 4;
+  g.out_bf16 = 0;
+  g.bias = w->logit_bias;
+  g.n_valid = d->E;
+  g.tiles_y = gemm_tiles_dense(d->T);
+  HIP_TRY(launch_gemm(g, f32 ? ELEM_F32 : ELEM_BF16, f32 ? 1 : 3, EPI_SUM, s));
+  GateArgs ga{ws.z, e_pad(d), d->T, d->E, d->k, d->gate, d->n_group, d->topk_group, d->per_group_k,
+              d->renorm, d->route_scale, idx, tw};
+  HIP_TRY(launch_gate(ga, s));
+  return MOE_OK;
+}
+
+moe_status run_quant_x(const moe_desc* d, const void* x, FfnWs& f, hipStream_t s) {
+  HIP_TRY(launch_quant_rows(x, 1, d->d, d->T, nullptr, 0, 0, f.qx, f.sx, s));
+  return MOE_OK;
+}
+
+struct FfnPlan {
+  const void* w13; const void* w2;
+  const float *s1, *s3, *s2;
+  int inter, groups;
+  const int32_t* offsets;      // routed only
+  int first;
+  const int32_t* sorted_slot;  // routed only
+  int rows_bound;              // routed: r_max; shared: T
+};
+
+moe_status run_ffn(const moe_desc* d, const FfnPlan& p, const void* x, const FfnWs& f, float* rows,
+                   hipStream_t s, hipEvent_t e1b, hipEvent_t e1e, hipEvent_t e2b, hipEvent_t e2e) {
+  const GemmElem el = weight_elem(d);
+  const int FB = frag_bytes_of(el);
+  const int KF = weight_kf(d);
+  const bool routed = p.offsets != nullptr;
+  const int tiles = routed ? gemm_tiles_bound(p.rows_bound, p.groups) : gemm_tiles_dense(d->T);
+
+  GemmArgs g1{};
+  g1.A = static_cast<const uint8_t*>(p.w13);
+  g1.a_group_stride = size_t(p.inter / 16) * (d->d / KF) * 2 * FB;
+  g1.K = d->d;
+  g1.N = p.inter;
+  g1.B = w8a8(d) ? reinterpret_cast<const uint8_t*>(f.qx) : static_cast<const uint8_t*>(x);
+  g1.ldb = size_t(d->d) * (w8a8(d) ? 1 : x_bytes(d));
+  g1.b_scale = w8a8(d) ? f.sx : nullptr;
+  g1.a_scale0 = w8a8(d) ? p.s1 : nullptr;
+  g1.a_scale1 = w8a8(d) ? p.s3 : nullptr;
+  g1.a_scale_stride = routed ? p.inter : 0;
+  g1.offsets = p.offsets;
+  g1.first = p.first;
+  g1.n_groups = p.groups;
+  g1.dense_rows = d->T;
+  g1.sorted_slot = p.sorted_slot;
+  g1.k = d->k;
+  g1.out = f.h;
+  g1.ldo = size_t(p.inter) * h_bytes(d);
+  g1.out_bf16 = d->dtype == MOE_DTYPE_BF16;
+  g1.tiles_y = tiles;
+  if (e1b) HIP_TRY(hipEventRecord(e1b, s));
+  HIP_TRY(launch_gemm(g1, el, 2, EPI_SWIGLU, s));
+  if (e1e) HIP_TRY(hipEventRecord(e1e, s));
+
+  if (w8a8(d)) {
+    HIP_TRY(launch_quant_rows(f.h, 0, p.inter, p.rows_bound, p.offsets, p.first, p.groups, f.qh, f.sh, s));
+  }
+
+  GemmArgs g2{};
+  g2.A = static_cast<const uint8_t*>(p.w2);
+  g2.a_group_stride = size_t(d->d / 16) * (p.inter / KF) * FB;
+  g2.K = p.inter;
+  g2.N = d->d;
+  g2.B = w8a8(d) ? reinterpret_cast<const uint8_t*>(f.qh) : f.h;
+  g2.ldb = size_t(p.inter) * (w8a8(d) ? 1 : h_bytes(d));
+  g2.b_scale = w8a8(d) ? f.sh : nullptr;
+  g2.a_scale0 = w8a8(d) ? p.s2 : nullptr;
+  g2.a_scale_stride = routed ? d->d : 0;
+  g2.offsets = p.offsets;
+  g2.first = p.first;
+  g2.n_groups = p.groups;
+  g2.dense_rows = d->T;
+  g2.sorted_slot = nullptr;
+  g2.out = reinterpret_cast<uint8_t*>(rows);
+  g2.ldo = size_t(d->d) * 4;
+  g2.out_bf16 = 0;
+  g2.tiles_y = tiles;
+  if (e2b) HIP_TRY(hipEventRecord(e2b, s));
+  HIP_TRY(launch_gemm(g2, el, 1, EPI_SUM, s));
+  if (e2e) HIP_TRY(hipEventRecord(e2e, s));
+  return MOE_OK;
+}
+
+FfnPlan routed_plan(const moe_desc* d, const moe_weights* w, const int32_t* offsets, const int32_t* ss) {
+  return FfnPlan{w->w13, w->w2, w->s1, w->s3, w->s2, d->inter, d->n_ffn, offsets, d->ffn_begin, ss, r_max(d)};
+}
+FfnPlan shared_plan(const moe_desc* d, const moe_weights* w) {
+  return FfnPlan{w->sw13, w->sw2, w->ss1, w->ss3, w->ss2, d->shared_inter, 1, nullptr, 0, nullptr, d->T};
+}
+
+bool routed_weights_ok(const moe_desc* d, const moe_weights* w) {
+  if (d->n_ffn == 0) return true;
+  if (!w->w13 || !w->w2) return false;
+  if (w8a8(d) && (!w->s1 || !w->s3 || !w->s2)) return false;
+  return true;
+}
+bool shared_weights_ok(const moe_desc* d, const moe_weights* w) {
+  if (d->shared_inter == 0) return true;
+  if (!w->sw13 || !w->sw2) return false;
+  if (w8a8(d) && (!w->ss1 || !w->ss3 || !w->ss2)) return false;
+  return true;
+}
+
+CombineArgs combine_args(const moe_desc* d, const void* x, const float* rows, const float* shared_rows,
+                         const int32_t* idx, const float* tw, const int32_t* offsets, const int32_t* slot_pos,
+                         void* y) {
+  CombineArgs c{};
+  c.x = x;
+  c.x_bf16 = d->dtype != MOE_DTYPE_F32;
+  c.rows = rows;
+  c.shared_rows = shared_rows;
+  c.topk_idx = idx;
+  c.topk_w = tw;
+  c.offsets = offsets;
+  c.slot_pos = slot_pos;
+  c.T = d->T;
+  c.d = d->d;
+  c.k = d->k;
+  c.ffn_begin = d->ffn_begin;
+  c.n_ffn = d->n_ffn;
+  c.zero_begin = d->zero_begin;
+  c.n_zero = d->n_zero;
+  c.y = y;
+  return c;
+}
+
+size_t ws_bytes_of(const moe_desc* d, int op) {
+  Carve c(nullptr);
+  switch (op) {
+    case MOE_OP_ROUTE_TOPK: carve_route(c, d); break;
+    case MOE_OP_PERMUTE: break;
+    case MOE_OP_FFN_ROUTED: {
+      FfnWs f{};
+      carve_qx(c, d, f);
+      carve_h(c, d, r_max(d), d->inter, f);
+      break;
+    }
+    case MOE_OP_FFN_SHARED: {
+      FfnWs f{};
+      carve_qx(c, d, f);
+      carve_h(c, d, d->T, d->shared_inter, f);
+      break;
+    }
+    case MOE_OP_COMBINE: break;
+    case MOE_OP_LAYER: carve_layer(c, d); break;
+    default: return 0;
+  }
+  return c.used;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t moe_workspace_bytes(const moe_desc* desc, int op) {
+  if (validate(desc) != MOE_OK) return 0;
+  return ws_bytes_of(desc, op);
+}
+
+const char* moe_status_str(moe_status status) {
+  switch (status) {
+    case MOE_OK: return "MOE_OK";
+    case MOE_ERR_INVALID_ARG: return "MOE_ERR_INVALID_ARG";
+    case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED";
+    case MOE_ERR_WORKSPACE: return "MOE_ERR_WORKSPACE";
+    case MOE_ERR_HIP: return "MOE_ERR_HIP";
+    default: return "MOE_ERR_UNKNOWN";
+  }
+}
+
+size_t moe_packed_bytes(const moe_desc* d, int part) {
+  if (validate(d) != MOE_OK) return 0;
+  const size_t wb = size_t(w_bytes(d));
+  switch (part) {
+    case MOE_PACK_ROUTER:
+      return d->dtype == MOE_DTYPE_F32 ? size_t(e_pad(d)) * d->d * 4 : size_t(e_pad(d)) * d->d * 3 * 2;
+    case MOE_PACK_W13: return size_t(d->n_ffn) * d->d * d->inter * 2 * wb;
+    case MOE_PACK_W2: return size_t(d->n_ffn) * d->d * d->inter * wb;
+    case MOE_PACK_SW13: return size_t(d->d) * d->shared_inter * 2 * wb;
+    case MOE_PACK_SW2: return size_t(d->d) * d->shared_inter * wb;
+    default: return 0;
+  }
+}
+
+moe_status moe_pack_weights(const moe_desc* d, int part, const void* src_a, const void* src_b, void* dst,
+                            size_t dst_bytes, void* stream) {
+  moe_status st = validate(d);
+  if (st != MOE_OK) return st;
+  if (part < MOE_PACK_ROUTER || part > MOE_PACK_SW2) return MOE_ERR_INVALID_ARG;
+  const size_t need = moe_packed_bytes(d, part);
+  if (need == 0) return MOE_OK;
+  if (!src_a || !dst) return MOE_ERR_INVALID_ARG;
+  if ((part == MOE_PACK_W13 || part == MOE_PACK_SW13) && !src_b) return MOE_ERR_INVALID_ARG;
+  if (dst_bytes < need) return MOE_ERR_WORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const GemmElem el = weight_elem(d);
+  hipError_t e = hipSuccess;
+  switch (part) {
+    case MOE_PACK_ROUTER:
+      e = launch_pack_router(static_cast<const float*>(src_a), d->dtype == MOE_DTYPE_F32 ? ELEM_F32 : ELEM_BF16,
+                             d->d, d->E, dst, s);
+      break;
+    case MOE_PACK_W13: e = launch_pack_experts(src_a, src_b, 2, el, d->n_ffn, d->d, d->inter, dst, s); break;
+    case MOE_PACK_W2: e = launch_pack_experts(src_a, nullptr, 1, el, d->n_ffn, d->inter, d->d, dst, s); break;
+    case MOE_PACK_SW13: e = launch_pack_experts(src_a, src_b, 2, el, 1, d->d, d->shared_inter, dst, s); break;
+    case MOE_PACK_SW2: e = launch_pack_experts(src_a, nullptr, 1, el, 1, d->shared_inter, d->d, dst, s); break;
+  }
+  return e == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
+moe_status moe_route_topk(const moe_desc* d, const moe_weights* w, const void* x, int32_t* topk_idx,
+                          float* topk_w, void* ws, size_t ws_bytes, void* stream) {
+  moe_status st = validate(d);
+  if (st != MOE_OK) return st;
+  if (!w || !w->router || !topk_idx || !topk_w || (!x && d->T > 0)) return MOE_ERR_INVALID_ARG;
+  const size_t need = ws_bytes_of(d, MOE_OP_ROUTE_TOPK);
+  if (ws_bytes < need || (need > 0 && !ws)) return MOE_ERR_WORKSPACE;
+  if (d->T == 0) return MOE_OK;
+  Carve c(ws);
+  const RouteWs r = carve_route(c, d);
+  return run_route(d, w, x, topk_idx, topk_w, r, static_cast<hipStream_t>(stream));
+}
+
+moe_status moe_permute(const moe_desc* d, const int32_t* topk_idx, int32_t* counts, int32_t* offsets,
+                       int32_t* sorted_slot, int32_t* slot_pos, void* ws, size_t ws_bytes, void* stream) {
+  (void)ws;
+  (void)ws_bytes;
+  moe_status st = validate(d);
+  if (st != MOE_OK) return st;
+  if (!counts || !offsets) return MOE_ERR_INVALID_ARG;
+  if (d->T > 0 && (!topk_idx || !sorted_slot || !slot_pos)) return MOE_ERR_INVALID_ARG;
+  return launch_permute(topk_idx, d->T * d->k, d->E, counts, offsets, sorted_slot, slot_pos,
+                        static_cast<hipStream_t>(stream)) == hipSuccess
+             ? MOE_OK
+             : MOE_ERR_HIP;
+}
+
+moe_status moe_grouped_ffn(const moe_desc* d, const moe_weights* w, int which, const void* x,
+                           const int32_t* offsets, const int32_t* sorted_slot, float* rows, void* ws,
+                           size_t ws_bytes, void* stream) {
+  moe_status st = validate(d);
+  if (st != MOE_OK) return st;
+  if (!w || (which != MOE_FFN_ROUTED && which != MOE_FFN_SHARED)) return MOE_ERR_INVALID_ARG;
+  const bool routed = which == MOE_FFN_ROUTED;
+  if (routed ? d->n_ffn == 0 : d->shared_inter == 0) return MOE_OK;   // nothing to compute
+  if (d->T == 0) return MOE_OK;
+  if (!x || !rows) return MOE_ERR_INVALID_ARG;
+  if (routed && (!offsets || !sorted_slot || !routed_weights_ok(d, w))) return MOE_ERR_INVALID_ARG;
+  if (!routed && !shared_weights_ok(d, w)) return MOE_ERR_INVALID_ARG;
+  const size_t need = ws_bytes_of(d, routed ? MOE_OP_FFN_ROUTED : MOE_OP_FFN_SHARED);
+  if (ws_bytes < need || !ws) return MOE_ERR_WORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  Carve c(ws);
+  FfnWs f{};
+  carve_qx(c, d, f);
+  carve_h(c, d, routed ? r_max(d) : d->T, routed ? d->inter : d->shared_inter, f);
+  if (w8a8(d)) {
+    st = run_quant_x(d, x, f, s);
+    if (st != MOE_OK) return st;
+  }
+  const FfnPlan p = routed ? routed_plan(d, w, offsets, sorted_slot) : shared_plan(d, w);
+  return run_ffn(d, p, x, f, rows, s, nullptr, nullptr, nullptr, nullptr);
+}
+
+moe_status moe_combine(const moe_desc* d, const void* x, const float* rows, const float* shared_rows,
+                       const int32_t* topk_idx, const float* topk_w, const int32_t* offsets,
+                       const int32_t* slot_pos, void* y, void* stream) {
+  moe_status st = validate(d);
+  if (st != MOE_OK) return st;
+  if (d->T == 0) return MOE_OK;
+  if (!x || !topk_idx || !topk_w || !y) return MOE_ERR_INVALID_ARG;
+  if (d->n_ffn > 0 && (!rows || !offsets || !slot_pos)) return MOE_ERR_INVALID_ARG;
+  if (d->shared_inter > 0 && !shared_rows) return MOE_ERR_INVALID_ARG;
+  const CombineArgs c = combine_args(d, x, rows, d->shared_inter > 0 ? shared_rows : nullptr, topk_idx, topk_w,
+                                     offsets, slot_pos, y);
+  return launch_combine(c, static_cast<hipStream_t>(stream)) == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
+moe_status moe_layer(const moe_desc* d, const moe_weights* w, const void* x, void* y, moe_aux* aux, void* ws,
+                     size_t ws_bytes, void* stream) {
+  moe_status st = validate(d);
+  if (st != MOE_OK) return st;
+  if (!w || !w->router || !routed_weights_ok(d, w) || !shared_weights_ok(d, w)) return MOE_ERR_INVALID_ARG;
+  if (d->T > 0 && (!x || !y)) return MOE_ERR_INVALID_ARG;
+  const size_t need = ws_bytes_of(d, MOE_OP_LAYER);
+  if (ws_bytes < need || !ws) return MOE_ERR_WORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  Carve c(ws);
+  LayerWs L = carve_layer(c, d);
+  moe_aux none{};
+  const moe_aux& A = aux ? *aux : none;
+  int32_t* idx = A.topk_idx ? A.topk_idx : L.idx;
+  float* tw = A.topk_w ? A.topk_w : L.w;
+  int32_t* counts = A.counts ? A.counts : L.counts;
+  int32_t* offsets = A.offsets ? A.offsets : L.offsets;
+  int32_t* sorted_slot = A.sorted_slot ? A.sorted_slot : L.sorted_slot;
+  int32_t* slot_pos = A.slot_pos ? A.slot_pos : L.slot_pos;
+  if (A.q_x) L.routed.qx = L.shared.qx = A.q_x;
+  if (A.s_x) L.routed.sx = L.shared.sx = A.s_x;
+
+  if (d->T > 0) {
+    st = run_route(d, w, x, idx, tw, L.route, s);
+    if (st != MOE_OK) return st;
+  }
+  HIP_TRY(launch_permute(idx, d->T * d->k, d->E, counts, offsets, sorted_slot, slot_pos, s));
+  if (d->T == 0) return MOE_OK;
+  if (w8a8(d)) {
+    st = run_quant_x(d, x, L.routed, s);
+    if (st != MOE_OK) return st;
+  }
+  if (d->n_ffn > 0) {
+    st = run_ffn(d, routed_plan(d, w, offsets, sorted_slot), x, L.routed, L.rows, s,
+                 static_cast<hipEvent_t>(A.ev_ffn1_begin), static_cast<hipEvent_t>(A.ev_ffn1_end),
+                 static_cast<hipEvent_t>(A.ev_ffn2_begin), static_cast<hipEvent_t>(A.ev_ffn2_end));
+    if (st != MOE_OK) return st;
+  }
+  if (d->shared_inter > 0) {
+    st = run_ffn(d, shared_plan(d, w), x, L.shared, L.shared_rows, s, nullptr, nullptr, nullptr, nullptr);
+    if (st != MOE_OK) return st;
+  }
+  const CombineArgs cb = combine_args(d, x, L.rows, L.shared_rows, idx, tw, offsets, slot_pos, y);
+  HIP_TRY(launch_combine(cb, s));
+  return MOE_OK;
+}
+
+}  // extern "C"

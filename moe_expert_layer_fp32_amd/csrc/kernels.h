@@ -1,0 +1,116 @@
+// Host-side launch interface of the gfx950 kernels (one translation unit per
+// kernel family; the C ABI in api.cpp drives them).
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace moe {
+
+// ---------------------------------------------------------------------------
+// Grouped-row matrix-core product (gemm.hip).
+//
+// out[row][col] = sum_k B[brow(row)][k] * W_g[k][col] for the rows of each
+// group g, with W_g packed as fragments [N/16][K/KF][S][64 lanes][BPL bytes].
+// Groups: either one dense group of `dense_rows` rows, or the resident
+// experts g = 0..n_groups-1 whose rows are the sorted rows
+// [offsets[first+g], offsets[first+g+1]) (written compacted at
+// row - offsets[first]). The B row of a sorted row is its token
+// sorted_slot[row] / k (gather) or its compacted index.
+// ---------------------------------------------------------------------------
+enum GemmElem : int { ELEM_F32 = 0, ELEM_BF16 = 1, ELEM_I8 = 2 };
+enum GemmEpi : int {
+  EPI_SWIGLU = 0,  // S = 2 (W1, W3): out = silu(a) * b
+  EPI_SUM = 1,     // S planes accumulated: out = acc (+ bias)
+};
+
+struct GemmArgs {
+  const uint8_t* A;          // packed weights
+  size_t a_group_stride;     // bytes between groups
+  int K, N;                  // reduction length, output columns (multiple of 16)
+  const uint8_t* B;          // activation rows
+  size_t ldb;                // bytes between B rows
+  const float* b_scale;      // int8: scale of each B row (indexed like B rows)
+  const float* a_scale0;     // int8: per-column scale of plane 0, [G][a_scale_stride]
+  const float* a_scale1;     // int8: per-column scale of plane 1 (SwiGLU)
+  int a_scale_stride;
+  const int* offsets;        // grouped rows when non-null
+  int first, n_groups;
+  int dense_rows;            // rows of the single dense group (offsets == null)
+  const int* sorted_slot;    // gather B rows by token when non-null
+  int k;
+  uint8_t* out;              // output rows
+  size_t ldo;                // bytes between output rows
+  int out_bf16;              // 1: bf16 out, 0: fp32 out
+  const float* bias;         // EPI_SUM: + bias[col] for col < n_valid
+  int n_valid;
+  int tiles_y;               // m-tile slots in the grid
+};
+
+hipError_t launch_gemm(const GemmArgs& a, GemmElem elem, int planes, GemmEpi epi,
+                       hipStream_t stream);
+
+// Upper bound on the m-tiles of grouped rows (R rows over G groups), and the
+// m-tiles of one dense group of `rows` rows.
+int gemm_tiles_bound(int max_rows, int n_groups);
+int gemm_tiles_dense(int rows);
+
+// ---------------------------------------------------------------------------
+// Gating + top-k (route.hip)
+// ---------------------------------------------------------------------------
+struct GateArgs {
+  const float* z;   // [T][ldz] logits, bias included
+  int ldz;
+  int T, E, k, gate, n_group, topk_group, per_group_k, renorm;
+  float route_scale;
+  int* topk_idx;
+  float* topk_w;
+};
+hipError_t launch_gate(const GateArgs& a, hipStream_t stream);
+
+// ---------------------------------------------------------------------------
+// Stable counting sort of slots by expert (permute.hip)
+// ---------------------------------------------------------------------------
+hipError_t launch_permute(const int* topk_idx, int n_slots, int E, int* counts, int* offsets,
+                          int* sorted_slot, int* slot_pos, hipStream_t stream);
+
+// ---------------------------------------------------------------------------
+// Per-row int8 quantisation (quant.hip). rows = fixed count, or (when
+// offsets != null) offsets[first + n_groups] - offsets[first] rows.
+// in_bf16: 1 for bf16 input rows, 0 for fp32.
+// ---------------------------------------------------------------------------
+hipError_t launch_quant_rows(const void* in, int in_bf16, int cols, int max_rows,
+                             const int* offsets, int first, int n_groups, int8_t* q, float* s,
+                             hipStream_t stream);
+
+// ---------------------------------------------------------------------------
+// Combine (combine.hip)
+// ---------------------------------------------------------------------------
+struct CombineArgs {
+  const void* x;             // [T][d] fp32 or bf16
+  int x_bf16;
+  const float* rows;         // compacted routed rows [R][d]
+  const float* shared_rows;  // [T][d] or null
+  const int* topk_idx;
+  const float* topk_w;
+  const int* offsets;        // [E+1]
+  const int* slot_pos;       // [T*k]
+  int T, d, k, ffn_begin, n_ffn, zero_begin, n_zero;
+  void* y;                   // [T][d] fp32 or bf16 (same type as x)
+};
+hipError_t launch_combine(const CombineArgs& a, hipStream_t stream);
+
+// ---------------------------------------------------------------------------
+// Weight packing (pack.hip)
+// ---------------------------------------------------------------------------
+// Expert weights [G][K][N] (element bytes es) from `planes` sources into
+// fragments [G][N/16][K/KF][planes][64][BPL].
+hipError_t launch_pack_experts(const void* src0, const void* src1, int planes, GemmElem elem,
+                               int G, int K, int N, void* dst, hipStream_t stream);
+// Router W_r [K][E] fp32 into fragments of ceil(E/16)*16 columns: one fp32
+// plane (elem = ELEM_F32) or three exact bf16 planes (elem = ELEM_BF16).
+hipError_t launch_pack_router(const float* wr, GemmElem elem, int K, int E, void* dst,
+                              hipStream_t stream);
+
+}  // namespace moe

@@ -265,9 +265,14 @@ def combine_outputs(inp: dict, cfg, X32: np.ndarray, idx: np.ndarray, w: np.ndar
             U[tj[:, 0], tj[:, 1]] = X32[tj[:, 0]]
         elif kind == "ffn":
             U[tj[:, 0], tj[:, 1]] = expert_ffn(inp, cfg, e - cfg.ffn_begin, X32[tj[:, 0]])
-    y = np.zeros((n, cfg.d), dtype=F64)
-    if cfg.shared_inter:
-        y += shared_ffn(inp, cfg, X32)
+    y_shared = shared_ffn(inp, cfg, X32) if cfg.shared_inter else None
+    return weighted_sum(U, w, y_shared)
+
+
+def weighted_sum(U: np.ndarray, w: np.ndarray, y_shared: np.ndarray | None) -> np.ndarray:
+    """Step 7: y_t = shared_t + sum_j w_tj U_tj (fp64, slots in order)."""
+    n, k, d = U.shape
+    y = np.zeros((n, d), dtype=F64) if y_shared is None else np.array(y_shared, dtype=F64)
     for j in range(k):
         y += np.asarray(w[:, j], F64)[:, None] * U[:, j]
     return y

@@ -1,0 +1,133 @@
+"""Helpers of the GPU parity tests: cached device layers, the routing
+comparison with near-tie exclusion, and the output error measures."""
+from __future__ import annotations
+
+import functools
+import json
+import math
+import os
+import sys
+
+import numpy as np
+import torch
+
+from moe_inputs import get, make_inputs
+from moe_inputs.gen import x_f32
+from oracle import moe_oracle as O
+
+U32 = 2.0 ** -24
+
+
+def say(*a):
+    """Name the case before a GPU step (flushed, so a crash still shows it)."""
+    print(*a, file=sys.stderr, flush=True)
+
+
+def record(**fields):
+    """Append measured figures to $MOE_PARITY_REPORT (JSON lines) when set."""
+    path = os.environ.get("MOE_PARITY_REPORT")
+    if path:
+        with open(path, "a") as f:
+            f.write(json.dumps(fields) + "\n")
+
+
+@functools.lru_cache(maxsize=2)
+def inputs(name: str, T: int | None = None, seed: int = 0):
+    cfg = get(name)
+    if T is not None:
+        cfg = cfg.replace(T=T)
+    return cfg, make_inputs(cfg, seed=seed)
+
+
+@functools.lru_cache(maxsize=1)
+def device_layer(name: str, T: int | None = None, seed: int = 0):
+    from moe_expert_layer_fp32_amd.layer import DeviceLayer
+    cfg, inp = inputs(name, T, seed)
+    say(f"[gpu] packing {cfg.name} T={cfg.T} seed={seed}")
+    return DeviceLayer(cfg, inp)
+
+
+def np_of(t: torch.Tensor) -> np.ndarray:
+    if t.dtype == torch.bfloat16:
+        t = t.float()
+    return t.detach().cpu().numpy()
+
+
+# ----------------------------------------------------------------------------
+# routing
+# ----------------------------------------------------------------------------
+def logit_error_bound(x64: np.ndarray, wr64: np.ndarray, z: np.ndarray, dtype: str) -> np.ndarray:
+    """Per-token bound on |z_gpu - z| used to call a decision a near-tie.
+
+    The GPU sums K = d products (three exact bf16 planes per weight for bf16
+    and W8A8 layers, 3d terms) in fp32. A rounding-error random walk gives
+    about sqrt(K) * 2^-24 * sqrt(sum_i (x_i W_ie)^2); the bound takes 16 times
+    that plus a few ulp of |z| for the final additions.
+    """
+    K = x64.shape[1] * (1 if dtype == "f32" else 3)
+    s2 = (x64 ** 2) @ (wr64 ** 2)
+    b = 16.0 * math.sqrt(K) * U32 * np.sqrt(s2) + 8.0 * U32 * np.abs(z)
+    return b.max(axis=1)
+
+
+def compare_routing(cfg, ref: dict, idx_gpu: np.ndarray, w_gpu: np.ndarray, x64, wr64,
+                    w_tol: float = 1e-5):
+    """Exact ids and weights within w_tol for every token whose decision is
+    clear of a tie; validity only for near-tie tokens. Returns the near-tie mask."""
+    bz = logit_error_bound(x64, wr64, ref["z"], cfg.dtype)
+    mz, mg = O.selection_margins(ref["z"], ref["scores"], cfg)
+    amb = (mz <= 2 * bz) | (mg <= 2 * (0.5 * bz + 1e-6))
+    clear = ~amb
+    bad = np.argwhere(idx_gpu[clear] != ref["idx"][clear])
+    assert bad.size == 0, (f"{bad.shape[0]} id mismatches on clear tokens; first token "
+                           f"{np.flatnonzero(clear)[bad[0][0]]}")
+    werr = np.abs(w_gpu[clear] - ref["w"][clear]).max() if clear.any() else 0.0
+    assert werr <= w_tol, f"gate weight error {werr}"
+    for t in np.flatnonzero(amb):
+        row = idx_gpu[t]
+        assert len(set(row.tolist())) == cfg.k and row.min() >= 0 and row.max() < cfg.E
+        if not cfg.topk_group and not cfg.per_group_k:
+            kth = np.sort(ref["z"][t])[::-1][cfg.k - 1]
+            assert np.all(ref["z"][t][row] >= kth - 2 * bz[t])
+    return amb
+
+
+# ----------------------------------------------------------------------------
+# outputs
+# ----------------------------------------------------------------------------
+def half_ulp(v: np.ndarray, out_dtype: str) -> np.ndarray:
+    """Half a unit in the last place of |v| in the output type."""
+    bits = 8 if out_dtype != "f32" else 24
+    a = np.maximum(np.abs(v), 2.0 ** -126)
+    return np.exp2(np.floor(np.log2(a)) - bits)
+
+
+def output_errors(y_gpu: np.ndarray, y_ref: np.ndarray, out_dtype: str):
+    """(literal, beyond_rounding): max|y_gpu - y_ref| / rms(y_ref), and the same
+    after allowing each element the half-ulp of rounding once to the output
+    type (the single rounding the definition itself ends with)."""
+    rms = float(np.sqrt(np.mean(y_ref ** 2)))
+    diff = np.abs(y_gpu - y_ref)
+    allow = half_ulp(np.maximum(np.abs(y_ref), np.abs(y_gpu)), out_dtype)
+    return float(diff.max() / rms), float(np.maximum(diff - allow, 0).max() / rms)
+
+
+TOL = {"f32": 1e-5, "bf16": 2e-2, "w8a8": 1e-2}
+
+
+def h_code_flip_allowance(h32: np.ndarray, sh: np.ndarray, q2: np.ndarray, s2: np.ndarray,
+                          eps: float = 1e-4) -> np.ndarray:
+    """Per-element allowance for int8 codes of h that sit within eps of a
+    half-integer boundary of h/s_h. The GPU computes h in fp32 (relative error
+    a few 1e-7, so at most ~1e-4 in code units); where the oracle's h lies that
+    close to a boundary the GPU may take the neighbouring code, which moves
+    output column n by exactly s_h * |q2[i, n]| * s2[n]. Returns that sum over
+    the near-tie codes of each row, shape [rows, d]."""
+    r = np.abs(h32.astype(np.float64) / np.where(sh > 0, sh, 1)[:, None])
+    near = np.abs(r - np.floor(r) - 0.5) < eps
+    q2abs = np.abs(q2.astype(np.float64))
+    return (near.astype(np.float64) @ q2abs) * sh[:, None].astype(np.float64) * s2[None, :]
+
+
+def x64_of(inp) -> np.ndarray:
+    return np.asarray(x_f32(inp), np.float64)

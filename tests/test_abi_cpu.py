@@ -1,0 +1,136 @@
+"""The C ABI on the CPU: libmoe.so loads, exports every symbol moe.h declares,
+and rejects bad arguments on the host before anything is launched (no call
+here reaches a GPU)."""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from moe_inputs import CONFIGS, get
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE = 0x10000   # never dereferenced: every call below fails validation first
+
+
+@pytest.fixture(scope="module")
+def L():
+    from moe_expert_layer_fp32_amd import lib
+    if not os.path.exists(lib.LIB_PATH):
+        pytest.fail("libmoe.so is not built (python -m moe_expert_layer_fp32_amd.build)")
+    lib.load_library()
+    return lib
+
+
+def header_functions():
+    text = open(os.path.join(ROOT, "include", "moe.h"), encoding="utf-8").read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function(L):
+    declared = header_functions()
+    assert set(declared) == set(L.EXPORTS), declared
+    lib = ctypes.CDLL(L.LIB_PATH)
+    for name in declared:
+        assert hasattr(lib, name), name
+
+
+def test_struct_sizes_match_header(L):
+    # 16 int32 + 1 float; 12 pointers; 12 pointers
+    assert ctypes.sizeof(L.MoeDesc) == 17 * 4
+    assert ctypes.sizeof(L.MoeWeights) == 12 * 8
+    assert ctypes.sizeof(L.MoeAux) == 12 * 8
+
+
+def test_status_strings(L):
+    assert L.moe_status_str(0) == "MOE_OK"
+    assert L.moe_status_str(-3) == "MOE_ERR_WORKSPACE"
+    assert L.moe_status_str(-99) == "MOE_ERR_UNKNOWN"
+
+
+@pytest.mark.parametrize("name", list(CONFIGS))
+def test_workspace_and_packed_sizes(L, name):
+    cfg = get(name)
+    d = L.desc_from_config(cfg)
+    assert L.moe_workspace_bytes(d, L.OP_LAYER) > 0
+    assert L.moe_workspace_bytes(d, L.OP_PERMUTE) == 0
+    wb = {"f32": 4, "bf16": 2, "w8a8": 1}[cfg.dtype]
+    assert L.moe_packed_bytes(d, L.PACK_W13) == cfg.n_ffn * cfg.d * cfg.inter * 2 * wb
+    assert L.moe_packed_bytes(d, L.PACK_W2) == cfg.n_ffn * cfg.d * cfg.inter * wb
+    assert L.moe_packed_bytes(d, L.PACK_SW13) == cfg.d * cfg.shared_inter * 2 * wb
+    ep = (cfg.E + 15) // 16 * 16
+    assert L.moe_packed_bytes(d, L.PACK_ROUTER) == ep * cfg.d * (4 if cfg.dtype == "f32" else 6)
+
+
+def _layer(L, d, ws_bytes=1 << 40, x=FAKE, y=FAKE, router=FAKE):
+    lib = L.load_library()
+    w = L.MoeWeights(router=router, w13=FAKE, w2=FAKE, s1=FAKE, s3=FAKE, s2=FAKE, sw13=FAKE, sw2=FAKE,
+                     ss1=FAKE, ss3=FAKE, ss2=FAKE)
+    return lib.moe_layer(ctypes.byref(d), ctypes.byref(w), x, y, None, FAKE, ws_bytes, None)
+
+
+def _desc(L, **kw):
+    cfg = get("dsv3_decode_share_bf16").replace(**kw)
+    return L.desc_from_config(cfg)
+
+
+BAD = [
+    (dict(k=300), -1),                             # k > E
+    (dict(gate="softmax"), 0),                     # control (valid; fails later on workspace only if too small)
+]
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("k", 257, -1), ("E", 0, -1), ("T", -1, -1), ("gate", 7, -1), ("dtype", 9, -1), ("n_group", 3, -1),
+    ("topk_group", 9, -1), ("per_group_k", 2, -1), ("ffn_begin", 250, -1), ("zero_begin", 4, None),
+    ("d", 7100, -2), ("inter", 2000, -2), ("shared_inter", 100, -2), ("E", 512, -2), ("k", 17, -2),
+    ("T", 1 << 18, -2),
+])
+def test_descriptor_validation(L, field, value, status):
+    d = _desc(L)
+    setattr(d, field, value)
+    if field == "zero_begin":        # identity ids overlapping the resident FFN ids
+        d.n_zero = 8
+        status = -1
+    if field == "E" and value == 512:
+        d.n_group = 8
+    assert _layer(L, d) == status
+    assert L.moe_workspace_bytes(d, L.OP_LAYER) == 0
+
+
+def test_group_limits(L):
+    d = _desc(L)
+    d.n_group, d.topk_group, d.E = 128, 4, 256      # > 64 groups with group-limited routing
+    assert _layer(L, d) == -2
+    d = L.desc_from_config(get("pangu_moge_w8a8"))
+    d.k = 6                                         # MoGE: k must be n_group * per_group_k
+    assert _layer(L, d) == -1
+
+
+def test_workspace_too_small_and_null_pointers(L):
+    d = _desc(L)
+    need = L.moe_workspace_bytes(d, L.OP_LAYER)
+    assert _layer(L, d, ws_bytes=need - 1) == -3
+    assert _layer(L, d, x=None) == -1
+    assert _layer(L, d, router=None) == -1
+    lib = L.load_library()
+    assert lib.moe_permute(ctypes.byref(d), FAKE, None, FAKE, FAKE, FAKE, None, 0, None) == -1
+    assert lib.moe_combine(ctypes.byref(d), FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, None) == -1
+    w = L.MoeWeights()
+    assert lib.moe_grouped_ffn(ctypes.byref(d), ctypes.byref(w), 0, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 40,
+                               None) == -1
+    assert lib.moe_grouped_ffn(ctypes.byref(d), ctypes.byref(w), 5, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 40,
+                               None) == -1
+    assert lib.moe_route_topk(ctypes.byref(d), ctypes.byref(w), FAKE, FAKE, FAKE, FAKE, 1 << 40, None) == -1
+
+
+def test_pack_rejects_small_destination(L):
+    d = _desc(L)
+    lib = L.load_library()
+    need = L.moe_packed_bytes(d, L.PACK_W13)
+    assert lib.moe_pack_weights(ctypes.byref(d), L.PACK_W13, FAKE, FAKE, FAKE, need - 1, None) == -3
+    assert lib.moe_pack_weights(ctypes.byref(d), L.PACK_W13, FAKE, None, FAKE, need, None) == -1
+    assert lib.moe_pack_weights(ctypes.byref(d), 99, FAKE, FAKE, FAKE, need, None) == -1

@@ -1,0 +1,427 @@
+"""GPU parity: every step of the HIP path (through the C ABI) against the CPU
+oracle on the same seeded inputs.
+
+Bars: routing tables bit-exact given the same ids; int8 activation codes
+bit-exact; gate weights within 1e-5; outputs within max|err|/rms of 1e-5
+(fp32), 2e-2 (bf16), 1e-2 (W8A8) beyond the single rounding to the output
+type (the literal measure is asserted too where rounding allows it). Tokens
+whose expert choice sits within rounding of a tie are checked for validity
+only.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import gpu_util as U
+from moe_inputs import get, make_inputs, make_routing
+from moe_inputs.configs import MoEConfig
+from moe_inputs.gen import bf16_to_f32
+from oracle import moe_oracle as O
+
+pytestmark = pytest.mark.gpu
+
+DECODE = ["tiny_fp32", "longcat_zero_bf16", "dsv3_decode_share_bf16", "pangu_moge_w8a8"]
+
+
+@pytest.fixture(autouse=True, scope="module")
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("needs a GPU")
+    from moe_expert_layer_fp32_amd import load_library
+    load_library()
+
+
+def _L():
+    from moe_expert_layer_fp32_amd import lib as L
+    from moe_expert_layer_fp32_amd.layer import DeviceLayer, to_device
+    return L, DeviceLayer, to_device
+
+
+# ----------------------------------------------------------------------------
+# packing
+# ----------------------------------------------------------------------------
+def _unpack_experts(buf: np.ndarray, G, K, N, S, elem_bytes, KF):
+    """Inverse of the fragment layout, written from its definition."""
+    per = KF // 4
+    dt = {4: np.float32, 2: np.uint16, 1: np.int8}[elem_bytes]
+    a = buf.view(dt).reshape(G, N // 16, K // KF, S, 4, 16, per)     # g nt kt s q r i
+    a = a.transpose(0, 3, 2, 4, 6, 1, 5)                              # g s kt q i nt r
+    return a.reshape(G, S, K, N)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "w8a8"])
+def test_pack_expert_fragments_roundtrip(dtype):
+    L, DeviceLayer, to_device = _L()
+    cfg = MoEConfig(name="pack", T=4, d=128, E=4, k=1, gate="softmax", n_ffn=3, inter=192,
+                    shared_inter=64, dtype=dtype)
+    inp = make_inputs(cfg)
+    U.say(f"[gpu] pack roundtrip {dtype}")
+    lay = DeviceLayer(cfg, inp)
+    KF = {"f32": 4, "bf16": 32, "w8a8": 64}[dtype]
+    eb = {"f32": 4, "bf16": 2, "w8a8": 1}[dtype]
+    w13 = _unpack_experts(lay.w13.cpu().numpy(), 3, 128, 192, 2, eb, KF)
+    assert np.array_equal(w13[:, 0], inp["w1"]) and np.array_equal(w13[:, 1], inp["w3"])
+    w2 = _unpack_experts(lay.w2.cpu().numpy(), 3, 192, 128, 1, eb, KF)
+    assert np.array_equal(w2[:, 0], inp["w2"])
+    sw13 = _unpack_experts(lay.sw13.cpu().numpy(), 1, 128, 64, 2, eb, KF)
+    assert np.array_equal(sw13[0, 0], inp["sw1"]) and np.array_equal(sw13[0, 1], inp["sw3"])
+
+
+@pytest.mark.parametrize("name", ["tiny_fp32", "longcat_zero_bf16", "dsv3_decode_share_bf16"])
+def test_router_planes_sum_exactly_to_router(name):
+    L, DeviceLayer, to_device = _L()
+    cfg = get(name).replace(n_ffn=0, n_zero=0, zero_begin=0, shared_inter=0, T=4)
+    inp = make_inputs(cfg)
+    U.say(f"[gpu] router planes {name}")
+    lay = DeviceLayer(cfg, inp)
+    buf = lay.router.cpu().numpy()
+    Ep = (cfg.E + 15) // 16 * 16
+    if cfg.dtype == "f32":
+        w = _unpack_experts(buf, 1, cfg.d, Ep, 1, 4, 4)[0, 0]
+        assert np.array_equal(w[:, :cfg.E], inp["w_router"]) and not w[:, cfg.E:].any()
+        return
+    planes = _unpack_experts(buf, 1, cfg.d, Ep, 3, 2, 32)[0]          # 3 x d x Ep bf16 bits
+    vals = bf16_to_f32(planes).astype(np.float64)
+    total = vals.sum(axis=0)
+    assert np.array_equal(total[:, :cfg.E], inp["w_router"].astype(np.float64))
+    # hi carries the leading bits: |mid| <= ulp(hi)/2, |lo| <= ulp(mid)/2
+    assert np.all(np.abs(vals[1]) <= np.abs(vals[0]) * 2.0 ** -8 + 1e-45)
+
+
+# ----------------------------------------------------------------------------
+# router + top-k
+# ----------------------------------------------------------------------------
+ROUTE_CASES = [("tiny_fp32", None), ("tiny_fp32", 333), ("longcat_zero_bf16", None),
+               ("dsv3_decode_share_bf16", None), ("pangu_moge_w8a8", None), ("prefill_zipf_bf16", 1024)]
+
+
+@pytest.mark.parametrize("name,T", ROUTE_CASES)
+def test_route_topk(name, T):
+    L, DeviceLayer, to_device = _L()
+    cfg = get(name).replace(n_ffn=0, n_zero=0, zero_begin=0, shared_inter=0)
+    if T:
+        cfg = cfg.replace(T=T)
+    inp = make_inputs(cfg)
+    U.say(f"[gpu] route_topk {name} T={cfg.T}")
+    lay = DeviceLayer(cfg, inp)
+    idx, w = lay.route_topk()
+    torch.cuda.synchronize()
+    ref = dict(zip(("z", "scores", "idx", "w"), O.route(inp, cfg)))
+    amb = U.compare_routing(cfg, ref, U.np_of(idx), U.np_of(w), U.x64_of(inp),
+                            inp["w_router"].astype(np.float64))
+    assert amb.mean() < 0.05
+
+
+def test_route_exact_ties_go_to_lower_id():
+    """Duplicated router columns give bit-identical logits on both sides; the
+    lower expert id must win every such tie."""
+    L, DeviceLayer, to_device = _L()
+    for gate in ("softmax", "sigmoid"):
+        cfg = MoEConfig(name="ties", T=96, d=256, E=32, k=6, gate=gate, dtype="bf16")
+        inp = make_inputs(cfg)
+        wr = inp["w_router"]
+        wr[:, 17] = wr[:, 3]
+        wr[:, 30] = wr[:, 9]
+        wr[:, 12] = wr[:, 5]
+        U.say(f"[gpu] exact ties {gate}")
+        lay = DeviceLayer(cfg, inp)
+        idx, w = lay.route_topk()
+        ref = dict(zip(("z", "scores", "idx", "w"), O.route(inp, cfg)))
+        got = U.np_of(idx)
+        for a, b in ((3, 17), (9, 30), (5, 12)):
+            # whenever both twins are chosen the lower id comes first; when only
+            # one is chosen it is the lower id
+            for t in range(cfg.T):
+                row = got[t].tolist()
+                if b in row:
+                    assert a in row and row.index(a) < row.index(b)
+        U.compare_routing(cfg, ref, got, U.np_of(w), U.x64_of(inp), wr.astype(np.float64))
+
+
+# ----------------------------------------------------------------------------
+# permute
+# ----------------------------------------------------------------------------
+def _permute_case(T, k, E, seed, skew=0.0):
+    cfg = MoEConfig(name="perm", T=T, d=64, E=E, k=k, gate="softmax", dtype="bf16")
+    idx, _ = make_routing(cfg, seed=seed, skew=skew)
+    return cfg, idx
+
+
+PERMUTE_CASES = [(256, 8, 96, 1, 0.0), (512, 8, 256, 2, 0.0), (456, 8, 64, 3, 0.0), (8192, 8, 256, 4, 1.1),
+                 (1, 1, 1, 5, 0.0), (1, 16, 16, 6, 0.0), (333, 3, 7, 7, 2.0), (65536, 16, 256, 8, 1.1)]
+
+
+@pytest.mark.parametrize("T,k,E,seed,skew", PERMUTE_CASES)
+def test_permute_bit_exact(T, k, E, seed, skew):
+    L, DeviceLayer, to_device = _L()
+    cfg, idx = _permute_case(T, k, E, seed, skew)
+    U.say(f"[gpu] permute T={T} k={k} E={E}")
+    d = L.desc_from_config(cfg)
+    ti = torch.from_numpy(idx).cuda()
+    counts = torch.empty(E, dtype=torch.int32, device="cuda")
+    offsets = torch.empty(E + 1, dtype=torch.int32, device="cuda")
+    ss = torch.empty(T * k, dtype=torch.int32, device="cuda")
+    sp = torch.empty(T * k, dtype=torch.int32, device="cuda")
+    L.moe_permute(d, ti, counts, offsets, ss, sp)
+    want = O.routing_tables(idx, E)
+    for got, ref, name in zip((counts, offsets, ss, sp), want, ("counts", "offsets", "sorted_slot", "slot_pos")):
+        assert np.array_equal(U.np_of(got), ref), name
+
+
+def test_permute_all_tokens_on_one_expert_and_empty_experts():
+    L, DeviceLayer, to_device = _L()
+    T, k, E = 1000, 3, 40
+    idx = np.stack([np.array([7, 0, 39])] * T).astype(np.int32)
+    cfg = MoEConfig(name="perm", T=T, d=64, E=E, k=k, gate="softmax", dtype="bf16")
+    U.say("[gpu] permute skewed")
+    counts, offsets, ss, sp = _run_permute(L, cfg, idx)
+    want = O.routing_tables(idx, E)
+    assert all(np.array_equal(a, b) for a, b in zip((counts, offsets, ss, sp), want))
+
+
+def _run_permute(L, cfg, idx):
+    T, k, E = cfg.T, cfg.k, cfg.E
+    ti = torch.from_numpy(np.ascontiguousarray(idx, dtype=np.int32)).cuda()
+    out = [torch.empty(n, dtype=torch.int32, device="cuda") for n in (E, E + 1, T * k, T * k)]
+    L.moe_permute(L.desc_from_config(cfg), ti, *out)
+    return [U.np_of(t) for t in out]
+
+
+def test_permute_drops_out_of_range_ids():
+    """Ids outside [0, E) are not counted and get slot_pos -1; the rest is the
+    stable sort of the valid slots (library routine: numpy stable argsort)."""
+    L, DeviceLayer, to_device = _L()
+    cfg, idx = _permute_case(300, 4, 32, 9)
+    idx = idx.copy()
+    idx[5, 1] = -1
+    idx[17, 3] = 32
+    idx[200, 0] = 1 << 20
+    U.say("[gpu] permute out-of-range ids")
+    counts, offsets, ss, sp = _run_permute(L, cfg, idx)
+    flat = idx.reshape(-1)
+    ok = (flat >= 0) & (flat < cfg.E)
+    valid_slots = np.flatnonzero(ok)
+    order = valid_slots[np.argsort(flat[ok], kind="stable")]
+    assert np.array_equal(counts, np.bincount(flat[ok], minlength=cfg.E))
+    assert offsets[-1] == ok.sum()
+    assert np.array_equal(ss[: ok.sum()], order)
+    assert np.all(sp[~ok] == -1)
+    assert np.array_equal(sp[order], np.arange(ok.sum()))
+
+
+# ----------------------------------------------------------------------------
+# grouped FFN (routed and shared) on a given routing
+# ----------------------------------------------------------------------------
+FFN_CASES = [("tiny_fp32", None, 0.0), ("longcat_zero_bf16", None, 0.0), ("dsv3_decode_share_bf16", None, 0.0),
+             ("pangu_moge_w8a8", None, 0.0), ("dsv3_decode_share_bf16", 300, 1.5)]
+
+
+def _expected_rows(cfg, inp, idx, tables):
+    """Oracle rows in sorted order, and (W8A8) the per-element allowance for
+    int8 codes of h that are near-ties."""
+    counts, offsets, ss, sp = tables
+    base = offsets[cfg.ffn_begin]
+    R = offsets[cfg.ffn_begin + cfg.n_ffn] - base
+    x = np.asarray(O.x_f32(inp), np.float32)
+    rows = np.zeros((R, cfg.d))
+    allow = np.zeros((R, cfg.d))
+    for el in range(cfg.n_ffn):
+        e = cfg.ffn_begin + el
+        r0, r1 = offsets[e], offsets[e + 1]
+        if r1 == r0:
+            continue
+        X = x[ss[r0:r1] // cfg.k]
+        if cfg.dtype == "w8a8":
+            u, parts = O.swiglu_w8a8(X, inp["w1"][el], inp["s1"][el], inp["w3"][el], inp["s3"][el],
+                                     inp["w2"][el], inp["s2"][el], return_parts=True)
+            allow[r0 - base:r1 - base] = U.h_code_flip_allowance(
+                parts["h"].astype(np.float32), parts["sh"], inp["w2"][el], inp["s2"][el])
+        else:
+            u = O.expert_ffn(inp, cfg, el, X)
+        rows[r0 - base:r1 - base] = u
+    return rows, allow
+
+
+@pytest.mark.parametrize("name,T,skew", FFN_CASES)
+def test_grouped_ffn_routed(name, T, skew):
+    L, DeviceLayer, to_device = _L()
+    cfg, inp = U.inputs(name, T)
+    lay = U.device_layer(name, T)
+    idx, _ = make_routing(cfg, seed=11, skew=skew)
+    U.say(f"[gpu] grouped_ffn routed {name} T={cfg.T} skew={skew}")
+    counts, offsets, ss, sp = lay.permute(torch.from_numpy(idx).cuda())
+    rows = lay.grouped_ffn(L.FFN_ROUTED, offsets, ss)
+    torch.cuda.synchronize()
+    tables = O.routing_tables(idx, cfg.E)
+    want, allow = _expected_rows(cfg, inp, idx, tables)
+    got = U.np_of(rows)[: want.shape[0]]
+    lit, _ = U.output_errors(got, want, "f32")
+    rms = float(np.sqrt(np.mean(want ** 2)))
+    beyond_flips = float(np.maximum(np.abs(got - want) - allow, 0).max() / rms)
+    U.record(test="grouped_ffn_routed", cfg=cfg.name, T=cfg.T, skew=skew, rows=int(want.shape[0]),
+             err_rows_literal=lit, err_rows_beyond_code_flips=beyond_flips,
+             rows_with_near_tie_codes=int((allow > 0).any(axis=1).sum()))
+    assert beyond_flips <= U.TOL[cfg.dtype], f"rows error {beyond_flips} (literal {lit})"
+
+
+@pytest.mark.parametrize("name", ["dsv3_decode_share_bf16", "pangu_moge_w8a8"])
+def test_grouped_ffn_shared(name):
+    L, DeviceLayer, to_device = _L()
+    cfg, inp = U.inputs(name)
+    lay = U.device_layer(name)
+    U.say(f"[gpu] grouped_ffn shared {name}")
+    rows = lay.grouped_ffn(L.FFN_SHARED)
+    X = np.asarray(O.x_f32(inp), np.float32)
+    allow = 0.0
+    if cfg.dtype == "w8a8":
+        want, parts = O.swiglu_w8a8(X, inp["sw1"], inp["ss1"], inp["sw3"], inp["ss3"], inp["sw2"], inp["ss2"],
+                                    return_parts=True)
+        allow = U.h_code_flip_allowance(parts["h"].astype(np.float32), parts["sh"], inp["sw2"], inp["ss2"])
+    else:
+        want = O.shared_ffn(inp, cfg, X)
+    got = U.np_of(rows)
+    lit, _ = U.output_errors(got, want, "f32")
+    beyond = float(np.maximum(np.abs(got - want) - allow, 0).max() / np.sqrt(np.mean(want ** 2)))
+    U.record(test="grouped_ffn_shared", cfg=cfg.name, T=cfg.T, err_rows_literal=lit,
+             err_rows_beyond_code_flips=beyond)
+    assert beyond <= U.TOL[cfg.dtype], f"shared rows error {beyond} (literal {lit})"
+
+
+# ----------------------------------------------------------------------------
+# combine on given rows
+# ----------------------------------------------------------------------------
+@pytest.mark.parametrize("name", ["tiny_fp32", "longcat_zero_bf16"])
+def test_combine(name):
+    L, DeviceLayer, to_device = _L()
+    cfg, inp = U.inputs(name)
+    lay = U.device_layer(name)
+    idx, w = make_routing(cfg, seed=21)
+    rng = np.random.default_rng(22)
+    R = cfg.T * cfg.k
+    rows = rng.standard_normal((R, cfg.d)).astype(np.float32)
+    shared = rng.standard_normal((cfg.T, cfg.d)).astype(np.float32)
+    U.say(f"[gpu] combine {name}")
+    counts, offsets, ss, sp = lay.permute(torch.from_numpy(idx).cuda())
+    y = lay.combine(torch.from_numpy(rows).cuda(), None, torch.from_numpy(idx).cuda(),
+                    torch.from_numpy(w).cuda(), offsets, sp)
+    _, off_ref, _, sp_ref = O.routing_tables(idx, cfg.E)
+    x = np.asarray(O.x_f32(inp), np.float64)
+    Uu = np.zeros((cfg.T, cfg.k, cfg.d))
+    for t in range(cfg.T):
+        for j in range(cfg.k):
+            e = idx[t, j]
+            kind = O.expert_kind(cfg, e)
+            if kind == "ffn":
+                Uu[t, j] = rows[sp_ref[t * cfg.k + j] - off_ref[cfg.ffn_begin]]
+            elif kind == "identity":
+                Uu[t, j] = x[t]
+    want = O.weighted_sum(Uu, w, None)
+    _, beyond = U.output_errors(U.np_of(y), want, cfg.dtype)
+    assert beyond <= 1e-6
+    del shared
+
+
+# ----------------------------------------------------------------------------
+# whole layer
+# ----------------------------------------------------------------------------
+LAYER_CASES = [("tiny_fp32", None), ("tiny_fp32", 333), ("longcat_zero_bf16", None), ("longcat_zero_bf16", 77),
+               ("dsv3_decode_share_bf16", None), ("dsv3_decode_share_bf16", 129), ("pangu_moge_w8a8", None)]
+
+
+def _check_layer(cfg, inp, lay, tokens=None):
+    y, t = lay.layer_with_tables()
+    torch.cuda.synchronize()
+    idx_gpu, w_gpu = U.np_of(t["topk_idx"]), U.np_of(t["topk_w"])
+    ref = O.moe_layer(inp, cfg, tokens=tokens)
+    sel = slice(None) if tokens is None else np.asarray(tokens)
+    x64 = U.x64_of(inp)[sel]
+    amb = U.compare_routing(cfg, ref, idx_gpu[sel], w_gpu[sel], x64, inp["w_router"].astype(np.float64))
+    assert amb.mean() < 0.05
+    clear = ~amb
+    y_gpu = U.np_of(y)[sel][clear]
+    lit, beyond = U.output_errors(y_gpu, ref["y"][clear], cfg.dtype)
+    U.say(f"    {cfg.name} T={cfg.T}: max|err|/rms literal {lit:.3e} beyond-rounding {beyond:.3e} "
+          f"near-tie tokens {int(amb.sum())}")
+    U.record(test="layer", cfg=cfg.name, T=cfg.T, sampled=None if tokens is None else len(tokens),
+             err_literal=lit, err_beyond_rounding=beyond, near_tie_tokens=int(amb.sum()))
+    assert beyond <= U.TOL[cfg.dtype]
+    # routing tables of the layer are the stable sort of its own ids
+    counts, offsets, ss, sp = (U.np_of(t[n]) for n in ("counts", "offsets", "sorted_slot", "slot_pos"))
+    flat = idx_gpu.reshape(-1)
+    assert np.array_equal(counts, np.bincount(flat, minlength=cfg.E))
+    assert np.array_equal(ss, np.argsort(flat, kind="stable"))
+    assert np.array_equal(sp[ss], np.arange(flat.size))
+    if tokens is None and not amb.any():
+        assert all(np.array_equal(a, b) for a, b in zip((counts, offsets, ss, sp),
+                                                          O.routing_tables(ref["idx"], cfg.E)))
+    if cfg.dtype == "w8a8":
+        q, s = O.quantise_rows(np.asarray(O.x_f32(inp), np.float32))
+        assert np.array_equal(U.np_of(t["q_x"]), q)
+        assert np.array_equal(U.np_of(t["s_x"]).view(np.uint32), s.view(np.uint32))
+    return y
+
+
+@pytest.mark.parametrize("name,T", LAYER_CASES)
+def test_layer(name, T):
+    cfg, inp = U.inputs(name, T)
+    lay = U.device_layer(name, T)
+    U.say(f"[gpu] layer {name} T={cfg.T}")
+    _check_layer(cfg, inp, lay)
+
+
+def test_layer_prefill_sampled_tokens():
+    """The full prefill workload (T 8192, 32 of 256 experts resident, Zipf
+    popularity) on the GPU, checked on 48 sampled tokens by the oracle."""
+    cfg, inp = U.inputs("prefill_zipf_bf16")
+    lay = U.device_layer("prefill_zipf_bf16")
+    U.say("[gpu] layer prefill_zipf_bf16 T=8192 (sampled)")
+    toks = np.random.default_rng(5).choice(cfg.T, 48, replace=False)
+    _check_layer(cfg, inp, lay, tokens=np.sort(toks))
+
+
+@pytest.mark.parametrize("name", ["longcat_zero_bf16", "dsv3_decode_share_bf16", "pangu_moge_w8a8"])
+def test_layer_is_deterministic(name):
+    cfg, inp = U.inputs(name)
+    lay = U.device_layer(name)
+    U.say(f"[gpu] determinism {name}")
+    a = lay.layer().clone()
+    b = lay.layer()
+    assert torch.equal(a.view(torch.int16) if a.dtype == torch.bfloat16 else a,
+                       b.view(torch.int16) if b.dtype == torch.bfloat16 else b)
+
+
+def test_layer_zero_tokens_is_a_noop():
+    L, DeviceLayer, to_device = _L()
+    lay = U.device_layer("longcat_zero_bf16")
+    x = lay.x[:0]
+    U.say("[gpu] layer T=0")
+    y = lay.layer(x)
+    torch.cuda.synchronize()
+    assert y.shape == (0, lay.cfg.d)
+
+
+def test_layer_single_token():
+    cfg, inp = U.inputs("dsv3_decode_share_bf16")
+    lay = U.device_layer("dsv3_decode_share_bf16")
+    U.say("[gpu] layer T=1")
+    for t in (0, 37):
+        y = lay.layer(lay.x[t:t + 1].contiguous())
+        ref = O.moe_layer(inp, cfg, tokens=[t])
+        _, beyond = U.output_errors(U.np_of(y), ref["y"], cfg.dtype)
+        assert beyond <= U.TOL[cfg.dtype]
+
+
+def test_layer_all_identity_experts():
+    """Every expert a zero-computation expert: y = route_scale * x, rounded once."""
+    L, DeviceLayer, to_device = _L()
+    cfg = MoEConfig(name="ident", T=100, d=256, E=16, k=4, gate="sigmoid", zero_begin=0, n_zero=16,
+                    route_scale=1.5, dtype="bf16")
+    inp = make_inputs(cfg)
+    U.say("[gpu] layer all identity")
+    lay = DeviceLayer(cfg, inp)
+    y = U.np_of(lay.layer())
+    want = 1.5 * np.asarray(O.x_f32(inp), np.float64)
+    _, beyond = U.output_errors(y, want, "bf16")
+    assert beyond <= 1e-5
