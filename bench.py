@@ -35,7 +35,8 @@ FP32_PEAK_TFLOPS = 157.3
 DEFAULT_CONFIG = "longcat_zero_bf16"
 METRIC = "MoE-layer tokens/s at 1 GPU; decode HBM GB/s %peak; prefill MFMA %peak"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "ffn1_traffic.json")
-KERNEL_SRC = os.path.join(ROOT, "moe_expert_layer_fp32_amd", "csrc", "gemm.hip")
+CSRC = os.path.join(ROOT, "moe_expert_layer_fp32_amd", "csrc")
+COPY_BYTES = 1 << 30
 
 
 def parse():
@@ -47,12 +48,52 @@ def parse():
     p.add_argument("--layers", type=int, default=0, help="layers cycled (0: enough for > 1 GB of weights)")
     p.add_argument("--cpu-seconds", type=float, default=10.0, help="target CPU time of the oracle sample")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="only run 5 device copies of 1 GiB (the known-size kernel for counter calibration)")
+    p.add_argument("--traffic", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "CAL_FETCH_CSV", "CAL_WRITE_CSV"),
+                   help="turn rocprofv3 --pmc counter_collection.csv files into the traffic record")
     return p.parse_args()
 
 
 def kernel_hash() -> str:
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """Hash of every kernel and host source of libmoe.so: counters taken on
+    one version do not describe another."""
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(CSRC)):
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(name.encode() + f.read())
+    return h.hexdigest()[:16]
+
+
+def counter_values(path: str) -> dict:
+    import csv
+    out: dict = {}
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            out.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+    return out
+
+
+def traffic_record(args, cfg_name: str) -> dict:
+    """HBM bytes per launch of the dominant kernel from FETCH_SIZE and
+    WRITE_SIZE (KiB per dispatch), each scaled by what the counter reads for a
+    device copy of COPY_BYTES bytes (read COPY_BYTES, write COPY_BYTES)."""
+    import statistics
+    fetch, write, cal_f, cal_w = (counter_values(p) for p in args)
+    copy = [k for k in cal_f if "copyBuffer" in k]
+    cf = statistics.median(cal_f[copy[0]]) * 1024.0
+    cw = statistics.median(cal_w[copy[0]]) * 1024.0
+    f_scale, w_scale = COPY_BYTES / cf, COPY_BYTES / cw
+    # the dominant kernel: the gate/up + SwiGLU instance with the most fetched bytes
+    cands = {k: v for k, v in fetch.items() if ("gemm_lds_kernel" in k or "gemm_rows_kernel" in k)
+             and (", 2, 0" in k)}
+    name = max(cands, key=lambda k: statistics.median(cands[k]))
+    fb = statistics.median(fetch[name]) * 1024.0 * f_scale
+    wb = statistics.median(write[name]) * 1024.0 * w_scale
+    return {"workload": cfg_name, "kernel": name, "kernel_sha": kernel_hash(),
+            "fetch_bytes_per_launch": fb, "write_bytes_per_launch": wb,
+            "bytes_per_launch": fb + wb, "fetch_scale": f_scale, "write_scale": w_scale,
+            "copy_bytes": COPY_BYTES}
 
 
 def ffn1_algorithmic(cfg, counts_per_layer):
@@ -104,6 +145,20 @@ def cpu_baseline(cfg, inp, seconds: float):
 
 def main() -> int:
     args = parse()
+    if args.traffic:
+        rec = traffic_record(args.traffic, args.config)
+        with open(TRAFFIC_FILE, "w") as f:
+            json.dump(rec, f, indent=1)
+        print(json.dumps(rec))
+        return 0
+    if args.copy_calibration:
+        import torch
+        src = torch.ones(COPY_BYTES, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        return 0
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the MoE layer here is one device's share and this "
               "build has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
@@ -174,7 +229,7 @@ def main() -> int:
         achieved = float(alg_bytes.mean()) / mean_s / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s"}
     roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
-    roof["kernel"] = "gemm_rows_kernel (routed gate/up + SwiGLU)"
+    roof["kernel"] = "routed-expert gate/up projection + SwiGLU (one launch per step)"
     roof["mean_us"] = round(mean_s * 1e6, 2)
     roof["alg_bytes_per_launch"] = int(alg_bytes.mean())
     roof["traffic"] = None

@@ -7,11 +7,17 @@
 #include <algorithm>
 #include <cmath>
 #include <cstdint>
+#include <climits>
 
 #include "kernels.h"
 #include "moe.h"
 
 using namespace moe;
+
+#define HIP_TRY(expr)                             \
+  do {                                            \
+    if ((expr) != hipSuccess) return MOE_ERR_HIP; \
+  } while (0)
 
 namespace {
 
@@ -40,6 +46,69 @@ GemmElem weight_elem(const moe_desc* d) {
 }
 int weight_kf(const moe_desc* d) { return d->dtype == MOE_DTYPE_F32 ? 4 : (d->dtype == MOE_DTYPE_BF16 ? 32 : 64); }
 int frag_bytes_of(GemmElem e) { return e == ELEM_F32 ? 64 * 4 : 64 * 16; }
+int kf_of(GemmElem e) { return e == ELEM_F32 ? 4 : (e == ELEM_BF16 ? 32 : 64); }
+GemmElem router_elem(const moe_desc* d) { return d->dtype == MOE_DTYPE_F32 ? ELEM_F32 : ELEM_BF16; }
+
+// ---------------------------------------------------------------------------
+// Which kernel runs each product (decided on the host from shapes only; the
+// per-expert part of the choice happens on the device).
+//  - Routed experts: the tiled LDS GEMM (see run_routed) whenever the shape
+//    tiles, else weight streaming (gemm_rows_kernel).
+//  - Dense products (router, shared expert): the tiled GEMM unless M is tiny
+//    or the shape does not tile; split-K when the tiles alone would give
+//    fewer than TARGET_WGS workgroups.
+// ---------------------------------------------------------------------------
+constexpr int PREFILL_T = 1024;
+constexpr int TARGET_WGS = 256;
+
+struct DensePlan {
+  bool lds;
+  LdsArgs L;
+  int tiles_y;
+  int tile_rows;
+  size_t partial_bytes;
+};
+
+DensePlan plan_dense(int M, int N, int K, GemmElem el, int nacc) {
+  DensePlan p{};
+  const int ch = lds_chunk_elems(el);
+  if (M <= 64 || K % ch != 0 || N % 32 != 0) {
+    p.lds = false;
+    p.tiles_y = gemm_tiles_dense(M, N, &p.tile_rows);
+    return p;
+  }
+  p.lds = true;
+  LdsArgs& L = p.L;
+  L.tile_rows = M >= 512 ? 128 : 64;
+  const int mt = ceil_div(M, L.tile_rows);
+  L.wave_features = (nacc == 1 && N % 256 == 0 && (N / 256) * mt >= TARGET_WGS) ? 64 : 32;
+  const int wgs = ceil_div(N, 4 * L.wave_features) * mt;
+  const int kc = K / ch;
+  int splits = 1;
+  if (wgs < TARGET_WGS) splits = std::max(1, std::min({ceil_div(TARGET_WGS, wgs), kc / 2, 8}));
+  L.splits = splits;
+  L.min_rows = 0;
+  L.max_rows = INT32_MAX;
+  L.part_rows = M;
+  p.tiles_y = mt;
+  p.partial_bytes = splits > 1 ? size_t(splits) * M * nacc * N * 4 : 0;
+  return p;
+}
+
+bool routed_tiled(const moe_desc* d, int N, int K) {
+  return K % lds_chunk_elems(weight_elem(d)) == 0 && N % 32 == 0;
+}
+
+// Split-K partial sums needed by any dense product of this layer.
+size_t dense_partial_bytes(const moe_desc* d, bool route, bool shared) {
+  size_t b = 0;
+  if (route) b = std::max(b, plan_dense(d->T, e_pad(d), d->d, router_elem(d), 1).partial_bytes);
+  if (shared && d->shared_inter > 0) {
+    b = std::max(b, plan_dense(d->T, d->shared_inter, d->d, weight_elem(d), 2).partial_bytes);
+    b = std::max(b, plan_dense(d->T, d->d, d->shared_inter, weight_elem(d), 1).partial_bytes);
+  }
+  return b;
+}
 
 moe_status validate(const moe_desc* d) {
   if (!d) return MOE_ERR_INVALID_ARG;
@@ -87,14 +156,18 @@ struct Carve {
   }
 };
 
-struct RouteWs { float* z; };
+struct RouteWs { float* z; void* partial; };
 RouteWs carve_route(Carve& c, const moe_desc* d) {
-  return {static_cast<float*>(c.take(size_t(d->T) * e_pad(d) * 4))};
+  RouteWs r;
+  r.z = static_cast<float*>(c.take(size_t(d->T) * e_pad(d) * 4));
+  r.partial = c.take(dense_partial_bytes(d, true, false));
+  return r;
 }
 
 struct FfnWs {
   int8_t* qx; float* sx;      // W8A8 activation codes (shared by routed and shared FFN)
   uint8_t* h; int8_t* qh; float* sh;
+  void* partial;              // split-K partial sums of dense products
 };
 void carve_qx(Carve& c, const moe_desc* d, FfnWs& f) {
   f.qx = nullptr; f.sx = nullptr;
@@ -110,6 +183,7 @@ void carve_h(Carve& c, const moe_desc* d, int rows, int inter, FfnWs& f) {
     f.qh = static_cast<int8_t*>(c.take(size_t(rows) * inter));
     f.sh = static_cast<float*>(c.take(size_t(rows) * 4));
   }
+  f.partial = nullptr;
 }
 
 struct LayerWs {
@@ -136,6 +210,7 @@ LayerWs carve_layer(Carve& c, const moe_desc* d) {
   L.rows = static_cast<float*>(c.take(size_t(r_max(d)) * d->d * 4));
   if (d->shared_inter > 0) {
     carve_h(c, d, d->T, d->shared_inter, L.shared);
+    L.shared.partial = c.take(dense_partial_bytes(d, false, true));
     L.shared_rows = static_cast<float*>(c.take(size_t(d->T) * d->d * 4));
   } else {
     L.shared_rows = nullptr;
@@ -146,10 +221,58 @@ LayerWs carve_layer(Carve& c, const moe_desc* d) {
 // ---------------------------------------------------------------------------
 // stages
 // ---------------------------------------------------------------------------
-#define HIP_TRY(expr)                                    \
-  do {                                                   \
-    if ((expr) != hipSuccess) return MOE_ERR_HIP;        \
-  } while (0)
+// Launch one dense product with its plan (tiled LDS GEMM or streaming).
+moe_status run_dense(GemmArgs g, int M, GemmElem el, int planes, GemmEpi epi, void* partial, hipStream_t s) {
+  const DensePlan p = plan_dense(M, g.N, g.K, el, epi == EPI_SWIGLU ? 2 : 1);
+  g.offsets = nullptr;
+  g.dense_rows = M;
+  g.tiles_y = p.tiles_y;
+  if (!p.lds) {
+    g.dense_tile_rows = p.tile_rows;
+    g.ksplit = gemm_stream_ksplit(g.N / 16, g.K / kf_of(el));
+    HIP_TRY(launch_gemm(g, el, planes, epi, s));
+    return MOE_OK;
+  }
+  LdsArgs L = p.L;
+  L.partial = partial;
+  HIP_TRY(launch_gemm_lds(g, L, el, planes, epi, s));
+  return MOE_OK;
+}
+
+// Launch one routed product. Shapes that tile go to the tiled kernel: at
+// decode sizes one launch with 64-row tiles (an expert with more rows takes
+// several); from PREFILL_T tokens up, experts with at most 64 rows use
+// 64-row tiles and bigger ones 128-row tiles (each weight fragment reused by
+// more rows). Few experts with long rows (fewer than TARGET_WGS tiled
+// workgroups, e.g. 8 resident experts of d 7168) and shapes that do not tile
+// stream through gemm_rows_kernel, whose wavefronts split the reduction.
+moe_status run_routed(GemmArgs g, const moe_desc* d, GemmElem el, int planes, GemmEpi epi, hipStream_t s) {
+  const long tiled_wgs = long(g.n_groups) * ceil_div(g.N, 128);
+  if (routed_tiled(d, g.N, g.K) && (tiled_wgs >= TARGET_WGS || d->T >= PREFILL_T)) {
+    LdsArgs L{};
+    L.wave_features = 32;
+    L.splits = 1;
+    L.part_rows = r_max(d);
+    L.tile_rows = 64;
+    L.min_rows = 1;
+    L.max_rows = d->T >= PREFILL_T ? 64 : INT32_MAX;
+    g.tiles_y = ceil_div(r_max(d), L.tile_rows) + g.n_groups;
+    HIP_TRY(launch_gemm_lds(g, L, el, planes, epi, s));
+    if (d->T >= PREFILL_T) {
+      L.tile_rows = 128;
+      L.min_rows = 65;
+      L.max_rows = INT32_MAX;
+      g.tiles_y = ceil_div(r_max(d), L.tile_rows) + g.n_groups;
+      HIP_TRY(launch_gemm_lds(g, L, el, planes, epi, s));
+    }
+    return MOE_OK;
+  }
+  g.max_group_rows = 0;
+  g.tiles_y = gemm_tiles_bound(r_max(d), g.n_groups);
+  g.ksplit = gemm_stream_ksplit(long(g.n_groups) * (g.N / 16), g.K / kf_of(el));
+  HIP_TRY(launch_gemm(g, el, planes, epi, s));
+  return MOE_OK;
+}
 
 moe_status run_route(const moe_desc* d, const moe_weights* w, const void* x, int32_t* idx, float* tw,
                      const RouteWs& ws, hipStream_t s) {
@@ -167,8 +290,8 @@ moe_status run_route(const moe_desc* d, const moe_weights* w, const void* x, int
   g.out_bf16 = 0;
   g.bias = w->logit_bias;
   g.n_valid = d->E;
-  g.tiles_y = gemm_tiles_dense(d->T);
-  HIP_TRY(launch_gemm(g, f32 ? ELEM_F32 : ELEM_BF16, f32 ? 1 : 3, EPI_SUM, s));
+  moe_status st = run_dense(g, d->T, f32 ? ELEM_F32 : ELEM_BF16, f32 ? 1 : 3, EPI_SUM, ws.partial, s);
+  if (st != MOE_OK) return st;
   GateArgs ga{ws.z, e_pad(d), d->T, d->E, d->k, d->gate, d->n_group, d->topk_group, d->per_group_k,
               d->renorm, d->route_scale, idx, tw};
   HIP_TRY(launch_gate(ga, s));
@@ -196,7 +319,7 @@ moe_status run_ffn(const moe_desc* d, const FfnPlan& p, const void* x, const Ffn
   const int FB = frag_bytes_of(el);
   const int KF = weight_kf(d);
   const bool routed = p.offsets != nullptr;
-  const int tiles = routed ? gemm_tiles_bound(p.rows_bound, p.groups) : gemm_tiles_dense(d->T);
+  moe_status st;
 
   GemmArgs g1{};
   g1.A = static_cast<const uint8_t*>(p.w13);
@@ -218,9 +341,9 @@ moe_status run_ffn(const moe_desc* d, const FfnPlan& p, const void* x, const Ffn
   g1.out = f.h;
   g1.ldo = size_t(p.inter) * h_bytes(d);
   g1.out_bf16 = d->dtype == MOE_DTYPE_BF16;
-  g1.tiles_y = tiles;
   if (e1b) HIP_TRY(hipEventRecord(e1b, s));
-  HIP_TRY(launch_gemm(g1, el, 2, EPI_SWIGLU, s));
+  st = routed ? run_routed(g1, d, el, 2, EPI_SWIGLU, s) : run_dense(g1, d->T, el, 2, EPI_SWIGLU, f.partial, s);
+  if (st != MOE_OK) return st;
   if (e1e) HIP_TRY(hipEventRecord(e1e, s));
 
   if (w8a8(d)) {
@@ -245,9 +368,9 @@ moe_status run_ffn(const moe_desc* d, const FfnPlan& p, const void* x, const Ffn
   g2.out = reinterpret_cast<uint8_t*>(rows);
   g2.ldo = size_t(d->d) * 4;
   g2.out_bf16 = 0;
-  g2.tiles_y = tiles;
   if (e2b) HIP_TRY(hipEventRecord(e2b, s));
-  HIP_TRY(launch_gemm(g2, el, 1, EPI_SUM, s));
+  st = routed ? run_routed(g2, d, el, 1, EPI_SUM, s) : run_dense(g2, d->T, el, 1, EPI_SUM, f.partial, s);
+  if (st != MOE_OK) return st;
   if (e2e) HIP_TRY(hipEventRecord(e2e, s));
   return MOE_OK;
 }
@@ -310,6 +433,7 @@ size_t ws_bytes_of(const moe_desc* d, int op) {
       FfnWs f{};
       carve_qx(c, d, f);
       carve_h(c, d, d->T, d->shared_inter, f);
+      c.take(dense_partial_bytes(d, false, true));
       break;
     }
     case MOE_OP_COMBINE: break;
@@ -425,6 +549,7 @@ moe_status moe_grouped_ffn(const moe_desc* d, const moe_weights* w, int which, c
   FfnWs f{};
   carve_qx(c, d, f);
   carve_h(c, d, routed ? r_max(d) : d->T, routed ? d->inter : d->shared_inter, f);
+  if (!routed) f.partial = c.take(dense_partial_bytes(d, false, true));
   if (w8a8(d)) {
     st = run_quant_x(d, x, f, s);
     if (st != MOE_OK) return st;

@@ -1,0 +1,456 @@
+// Tiled matrix-core GEMM for gfx950: the GEMM end of the per-expert
+// GEMV/GEMM switch (SwiftGMM's mode switch by load intensity, page
+// "华为技术披露集 VOL.12：昇腾×盘古", section SwiftGMM), used for experts and
+// dense problems with many rows (prefill experts, the shared expert, the
+// router at large T).
+//
+// Work split: a workgroup (4 wavefronts) owns BM rows x 4*NF output features
+// of one group (expert). The BM gathered activation rows are the shared
+// operand: they are staged through LDS in 256-byte-per-row chunks (double
+// buffered; the global loads of a chunk run two chunks ahead in registers),
+// rows padded by 16 bytes so the rows a 32x32 matrix-core operand reads land
+// in distinct banks. The weights are not shared between wavefronts (each
+// wavefront owns NF features), so they go straight from global memory into
+// a register ring 8 matrix-core steps deep, in the packed fragment layout: a
+// 32x32 operand is four 256-byte pieces of two adjacent 16-column fragments.
+// Each weight fragment is reused for BM rows.
+//
+// Split-K: when rows x features give too few workgroups to fill the device
+// (decode-sized shared expert), the reduction is cut into `splits` ranges;
+// each writes raw fp32 (int32 for int8) partial sums, and gemm_reduce_kernel
+// adds them in split order and applies the epilogue, so the result does not
+// depend on scheduling.
+#include <type_traits>
+
+#include "common.h"
+#include "kernels.h"
+
+namespace moe {
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef int i32x16 __attribute__((ext_vector_type(16)));
+
+struct M32BF16 {
+  using op_t = bf16x8;
+  using acc_t = f32x16;
+  using part_t = float;
+  static constexpr int KF = 32, KM = 16, BPL = 16, ESZ = 2;
+  __device__ static inline acc_t mfma(op_t a, op_t b, acc_t c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+  }
+  __device__ static inline op_t load(const uint8_t* p) {
+    return __builtin_bit_cast(op_t, *reinterpret_cast<const u32x4*>(p));
+  }
+};
+struct M32I8 {
+  using op_t = i32x4;
+  using acc_t = i32x16;
+  using part_t = int;
+  static constexpr int KF = 64, KM = 32, BPL = 16, ESZ = 1;
+  __device__ static inline acc_t mfma(op_t a, op_t b, acc_t c) {
+    return __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, c, 0, 0, 0);
+  }
+  __device__ static inline op_t load(const uint8_t* p) {
+    return __builtin_bit_cast(op_t, *reinterpret_cast<const u32x4*>(p));
+  }
+};
+struct M32F32 {
+  using op_t = float;
+  using acc_t = f32x16;
+  using part_t = float;
+  static constexpr int KF = 4, KM = 2, BPL = 4, ESZ = 4;
+  __device__ static inline acc_t mfma(op_t a, op_t b, acc_t c) {
+    return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+  }
+  __device__ static inline op_t load(const uint8_t* p) { return *reinterpret_cast<const float*>(p); }
+};
+
+constexpr int CH_BYTES = 256;              // bytes of one row per LDS chunk
+constexpr int LDS_ROW = CH_BYTES + 16;     // padded row stride (4-bank shift per row)
+
+__device__ inline float silu_f(float v) { return v / (1.0f + expf(-v)); }
+
+// Locate m-tile `tile` (rows per tile `tm`) among the groups whose row count
+// lies in [lo, hi]. Wave-uniform; false past the last tile.
+__device__ inline bool locate_tile_lds(const GemmArgs& a, int tile, int tm, int lo, int hi, int& g, int& row0,
+                                       int& nrows, int& out0) {
+  if (a.offsets == nullptr) {
+    g = 0;
+    row0 = tile * tm;
+    nrows = min(tm, a.dense_rows - row0);
+    out0 = row0;
+    return nrows > 0;
+  }
+  const int lane = threadIdx.x & (WAVE - 1);
+  const int base = a.offsets[a.first];
+  int cnt[4];
+  int local = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int gg = lane * 4 + i;
+    int c = 0;
+    if (gg < a.n_groups) {
+      const int n = a.offsets[a.first + gg + 1] - a.offsets[a.first + gg];
+      if (n >= lo && n <= hi) c = ceil_div(n, tm);
+    }
+    cnt[i] = c;
+    local += c;
+  }
+  int incl = local;
+#pragma unroll
+  for (int d = 1; d < WAVE; d <<= 1) {
+    const int v = __shfl_up(incl, d, WAVE);
+    if (lane >= d) incl += v;
+  }
+  const int excl = incl - local;
+  const uint64_t hit = __ballot(tile >= excl && tile < incl);
+  if (hit == 0) return false;
+  const int src = __builtin_ctzll(hit);
+  int my_g = -1, my_mt = 0;
+  if (lane == src) {
+    int t = tile - excl;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if (my_g < 0) {
+        if (t < cnt[i]) {
+          my_g = lane * 4 + i;
+          my_mt = t;
+        } else {
+          t -= cnt[i];
+        }
+      }
+    }
+  }
+  g = __shfl(my_g, src, WAVE);
+  const int mt = __shfl(my_mt, src, WAVE);
+  const int gbeg = a.offsets[a.first + g];
+  const int gend = a.offsets[a.first + g + 1];
+  row0 = gbeg + mt * tm;
+  nrows = min(tm, gend - row0);
+  out0 = row0 - base;
+  return true;
+}
+
+template <class Tr, int S, int EPI, int NF, int BM>
+__global__ __launch_bounds__(WG_THREADS) void gemm_lds_kernel(GemmArgs a, LdsArgs L) {
+  constexpr int FT = NF / 32;                  // 32-feature tiles per wavefront
+  constexpr int MBK = BM / 32;                 // 32-row blocks per tile
+  constexpr int FB = FRAG_LANES * Tr::BPL;     // packed fragment bytes
+  constexpr int CH_ELEMS = CH_BYTES / Tr::ESZ;
+  constexpr int CH_KT = CH_ELEMS / Tr::KF;     // packed reduction steps per chunk
+  constexpr int CH_KS = CH_ELEMS / Tr::KM;     // matrix-core steps per chunk
+  constexpr int NACC = (EPI == EPI_SWIGLU) ? 2 : 1;
+  constexpr int LOADS = BM * CH_BYTES / (WG_THREADS * 16);   // 16-byte B loads per thread per chunk
+  using op_t = typename Tr::op_t;
+  using acc_t = typename Tr::acc_t;
+
+  __shared__ __attribute__((aligned(16))) uint8_t lds[2][BM * LDS_ROW];
+  const int lane = threadIdx.x & (WAVE - 1);
+  const int wave = threadIdx.x / WAVE;
+
+  // XCD-aware linear block -> (column block, m-tile), m-tile fastest.
+  const int nbx = gridDim.x * gridDim.y;
+  const int b = blockIdx.y * gridDim.x + blockIdx.x;
+  const int q = nbx / 8;
+  const int logical = b < q * 8 ? (b % 8) * q + b / 8 : b;
+  const int tile = logical % a.tiles_y;
+  const int nblock = logical / a.tiles_y;
+  const int split = blockIdx.z;
+
+  int g, row0, nrows, out0;
+  if (!locate_tile_lds(a, tile, BM, L.min_rows, L.max_rows, g, row0, nrows, out0)) return;
+  g = __builtin_amdgcn_readfirstlane(g);
+  row0 = __builtin_amdgcn_readfirstlane(row0);
+  nrows = __builtin_amdgcn_readfirstlane(nrows);
+  out0 = __builtin_amdgcn_readfirstlane(out0);
+
+  const int KT = a.K / Tr::KF;
+  const int KC = a.K / CH_ELEMS;               // chunks in the whole reduction
+  const int c_begin = split * KC / L.splits;
+  const int c_end = (split + 1) * KC / L.splits;
+  const int nch = c_end - c_begin;
+
+  // ---- B staging: this thread's rows and byte column inside a chunk ----
+  const uint8_t* bsrc[LOADS];
+  int bdst[LOADS];
+#pragma unroll
+  for (int i = 0; i < LOADS; ++i) {
+    const int lin = threadIdx.x + i * WG_THREADS;
+    const int r = lin / (CH_BYTES / 16);
+    const int col = (lin % (CH_BYTES / 16)) * 16;
+    const int rr = min(r, nrows - 1);
+    const int brow = a.sorted_slot ? a.sorted_slot[row0 + rr] / a.k : out0 + rr;
+    bsrc[i] = a.B + size_t(brow) * a.ldb + size_t(c_begin) * CH_BYTES + col;
+    bdst[i] = r * LDS_ROW + col;
+  }
+  // Two register stages of chunk loads (parity of the chunk index).
+  u32x4 bstage[2][LOADS];
+  auto load_b = [&](int st, int c) {
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) bstage[st][i] = *reinterpret_cast<const u32x4*>(bsrc[i] + size_t(c) * CH_BYTES);
+  };
+  auto store_b = [&](int st, int buf) {
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) *reinterpret_cast<u32x4*>(&lds[buf][bdst[i]]) = bstage[st][i];
+  };
+
+  // ---- A: this wavefront's feature tiles, straight from global ----
+  // A wavefront past the last feature tile (N not a multiple of the block)
+  // computes a copy of the last tile and stores nothing.
+  const int ft_first = (nblock * WG_WAVES + wave) * FT;
+  const bool wave_live = ft_first * 32 < a.N;
+  const int ft0 = wave_live ? ft_first : a.N / 32 - FT;
+  const int r32 = lane & 31, half = lane >> 5;
+  const uint8_t* abase = a.A + size_t(g) * a.a_group_stride +
+                         size_t((2 * ft0 + (r32 >> 4)) * KT) * S * FB + (half * 16 + (r32 & 15)) * Tr::BPL;
+  // Ring of RA matrix-core steps of weight operands, refilled RA steps ahead
+  // across chunk boundaries. Every load is unconditional (steps past the end
+  // re-read the last one), so the waits only drain the step being used.
+  constexpr int RA = 8;
+  static_assert(CH_KS % RA == 0, "ring must divide the chunk");
+  op_t aring[RA][FT][S];
+  const int nsteps = nch * CH_KS;
+  auto load_a = [&](int slot, int i) {
+    const int kt = c_begin * CH_KT + (i >> 1);
+    const int h = i & 1;
+#pragma unroll
+    for (int f = 0; f < FT; ++f)
+#pragma unroll
+      for (int s = 0; s < S; ++s)
+        aring[slot][f][s] =
+            Tr::load(abase + (size_t(2 * f) * KT * S + size_t(kt) * S + s) * FB + h * 2 * 16 * Tr::BPL);
+  };
+
+  acc_t acc[NACC][FT][MBK];
+#pragma unroll
+  for (int s = 0; s < NACC; ++s)
+#pragma unroll
+    for (int f = 0; f < FT; ++f)
+#pragma unroll
+      for (int m = 0; m < MBK; ++m)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) acc[s][f][m][j] = 0;
+
+  // One chunk: matrix-core steps from LDS buffer `buf`, then the next chunk
+  // (loaded two chunks ago into register stage `st`) goes to the other
+  // buffer and that stage is refilled with the chunk after next.
+  auto chunk = [&](auto st_tag, int c) {
+    constexpr int st = decltype(st_tag)::value;
+    const int buf = c & 1;
+#pragma unroll
+    for (int ks = 0; ks < CH_KS; ++ks) {
+      const int slot = ks % RA;
+      op_t bf[MBK];
+#pragma unroll
+      for (int m = 0; m < MBK; ++m)
+        bf[m] = Tr::load(&lds[buf][(m * 32 + r32) * LDS_ROW + ks * (Tr::KM * Tr::ESZ) + half * Tr::BPL]);
+#pragma unroll
+      for (int f = 0; f < FT; ++f)
+#pragma unroll
+        for (int s = 0; s < S; ++s)
+#pragma unroll
+          for (int m = 0; m < MBK; ++m) {
+            const int sa = (EPI == EPI_SWIGLU) ? s : 0;
+            acc[sa][f][m] = Tr::mfma(aring[slot][f][s], bf[m], acc[sa][f][m]);
+          }
+      load_a(slot, min(c * CH_KS + ks + RA, nsteps - 1));
+    }
+    store_b(st, buf ^ 1);          // chunk c + 1 (a copy nobody reads after the last)
+    load_b(st, min(c + 3, nch - 1));
+    __syncthreads();
+  };
+
+  if (nch > 0) {
+    load_b(0, 0);
+    load_b(1, min(1, nch - 1));
+#pragma unroll
+    for (int r = 0; r < RA; ++r) load_a(r, min(r, nsteps - 1));
+    store_b(0, 0);
+    load_b(0, min(2, nch - 1));
+    __syncthreads();
+    // chunk c stores chunk c + 1 from stage (c + 1) & 1
+    int c = 0;
+    for (; c + 2 <= nch; c += 2) {
+      chunk(std::integral_constant<int, 1>{}, c);
+      chunk(std::integral_constant<int, 0>{}, c + 1);
+    }
+    if (c < nch) chunk(std::integral_constant<int, 1>{}, c);
+  }
+  if (!wave_live) return;
+
+  // ---- epilogue ----
+  // acc[.][f][m] element j: feature ft*32 + 8*(j/4) + 4*half + j%4, row m*32 + r32.
+#pragma unroll
+  for (int m = 0; m < MBK; ++m) {
+    const int r = m * 32 + r32;
+    if (r >= nrows) continue;
+    const int orow = out0 + r;
+    float bs = 1.f;
+    if (L.splits == 1 && a.b_scale) {
+      const int brow = a.sorted_slot ? a.sorted_slot[row0 + r] / a.k : orow;
+      bs = a.b_scale[brow];
+    }
+#pragma unroll
+    for (int f = 0; f < FT; ++f) {
+#pragma unroll
+      for (int jg = 0; jg < 4; ++jg) {
+        const int c0 = (ft0 + f) * 32 + 8 * jg + 4 * half;
+        if (L.splits > 1) {
+          // raw partial sums: [split][row][S * N], plane s at column s * N + c
+          typename Tr::part_t* P = reinterpret_cast<typename Tr::part_t*>(L.partial) +
+                                   (size_t(split) * L.part_rows + orow) * size_t(NACC) * a.N;
+#pragma unroll
+          for (int s = 0; s < NACC; ++s) {
+            typename Tr::part_t v4[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) v4[j] = acc[s][f][m][jg * 4 + j];
+            *reinterpret_cast<u32x4*>(P + size_t(s) * a.N + c0) = __builtin_bit_cast(u32x4, v4);
+          }
+          continue;
+        }
+        float v[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float cs0 = a.a_scale0 ? a.a_scale0[size_t(g) * a.a_scale_stride + c0 + j] : 1.f;
+          if (EPI == EPI_SWIGLU) {
+            const float cs1 = a.a_scale1 ? a.a_scale1[size_t(g) * a.a_scale_stride + c0 + j] : 1.f;
+            const float ga = float(acc[0][f][m][jg * 4 + j]) * bs * cs0;
+            const float up = float(acc[1][f][m][jg * 4 + j]) * bs * cs1;
+            v[j] = silu_f(ga) * up;
+          } else {
+            const float bias = (a.bias && c0 + j < a.n_valid) ? a.bias[c0 + j] : 0.f;
+            v[j] = float(acc[0][f][m][jg * 4 + j]) * bs * cs0 + bias;
+          }
+        }
+        uint8_t* op = a.out + size_t(orow) * a.ldo;
+        if (a.out_bf16) {
+          u32x2 pk;
+          pk[0] = uint32_t(f32_to_bf16(v[0])) | (uint32_t(f32_to_bf16(v[1])) << 16);
+          pk[1] = uint32_t(f32_to_bf16(v[2])) | (uint32_t(f32_to_bf16(v[3])) << 16);
+          *reinterpret_cast<u32x2*>(op + size_t(c0) * 2) = pk;
+        } else {
+          *reinterpret_cast<f32x4*>(op + size_t(c0) * 4) = f32x4{v[0], v[1], v[2], v[3]};
+        }
+      }
+    }
+  }
+}
+
+// Sum of the split partials in split order, then the epilogue of the
+// product. One thread per 4 output columns of one row; rows of the selected
+// groups only.
+template <typename PT, int EPI>
+__global__ __launch_bounds__(256) void gemm_reduce_kernel(GemmArgs a, LdsArgs L) {
+  constexpr int NACC = (EPI == EPI_SWIGLU) ? 2 : 1;
+  const int cols4 = a.N / 4;
+  const size_t idx = blockIdx.x * size_t(blockDim.x) + threadIdx.x;
+  const int orow = int(idx / cols4);
+  const int c0 = int(idx % cols4) * 4;
+  if (orow >= L.part_rows) return;
+  // Which group holds this compacted row, and is it one this product covered?
+  int g = 0, brow = orow;
+  if (a.offsets) {
+    const int base = a.offsets[a.first];
+    const int srow = orow + base;
+    if (srow >= a.offsets[a.first + a.n_groups]) return;
+    int lo = 0, hi = a.n_groups - 1;   // last group whose start <= srow
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) / 2;
+      if (a.offsets[a.first + mid] <= srow) lo = mid; else hi = mid - 1;
+    }
+    g = lo;
+    const int n = a.offsets[a.first + g + 1] - a.offsets[a.first + g];
+    if (n < L.min_rows || n > L.max_rows) return;
+    brow = a.sorted_slot ? a.sorted_slot[srow] / a.k : orow;
+  } else if (orow >= a.dense_rows) {
+    return;
+  }
+  float sum[NACC][4];
+#pragma unroll
+  for (int s = 0; s < NACC; ++s) {
+    PT t[4] = {0, 0, 0, 0};
+    for (int sp = 0; sp < L.splits; ++sp) {
+      const PT* P = reinterpret_cast<const PT*>(L.partial) + (size_t(sp) * L.part_rows + orow) * size_t(NACC) * a.N +
+                    size_t(s) * a.N + c0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) t[j] += P[j];
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) sum[s][j] = float(t[j]);
+  }
+  const float bs = a.b_scale ? a.b_scale[brow] : 1.f;
+  float v[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const float cs0 = a.a_scale0 ? a.a_scale0[size_t(g) * a.a_scale_stride + c0 + j] : 1.f;
+    if (EPI == EPI_SWIGLU) {
+      const float cs1 = a.a_scale1 ? a.a_scale1[size_t(g) * a.a_scale_stride + c0 + j] : 1.f;
+      v[j] = silu_f(sum[0][j] * bs * cs0) * (sum[1][j] * bs * cs1);
+    } else {
+      const float bias = (a.bias && c0 + j < a.n_valid) ? a.bias[c0 + j] : 0.f;
+      v[j] = sum[0][j] * bs * cs0 + bias;
+    }
+  }
+  uint8_t* op = a.out + size_t(orow) * a.ldo;
+  if (a.out_bf16) {
+    u32x2 pk;
+    pk[0] = uint32_t(f32_to_bf16(v[0])) | (uint32_t(f32_to_bf16(v[1])) << 16);
+    pk[1] = uint32_t(f32_to_bf16(v[2])) | (uint32_t(f32_to_bf16(v[3])) << 16);
+    *reinterpret_cast<u32x2*>(op + size_t(c0) * 2) = pk;
+  } else {
+    *reinterpret_cast<f32x4*>(op + size_t(c0) * 4) = f32x4{v[0], v[1], v[2], v[3]};
+  }
+}
+
+int lds_chunk_elems(GemmElem elem) { return CH_BYTES / (elem == ELEM_F32 ? 4 : (elem == ELEM_BF16 ? 2 : 1)); }
+
+template <class Tr, int S, int EPI, int NF, int BM>
+static hipError_t launch_lds_one(const GemmArgs& a, const LdsArgs& L, hipStream_t stream) {
+  const dim3 grid(ceil_div(a.N, WG_WAVES * NF), a.tiles_y, L.splits);
+  hipLaunchKernelGGL((gemm_lds_kernel<Tr, S, EPI, NF, BM>), grid, dim3(WG_THREADS), 0, stream, a, L);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || L.splits == 1) return e;
+  const size_t threads = size_t(L.part_rows) * (a.N / 4);
+  hipLaunchKernelGGL((gemm_reduce_kernel<typename Tr::part_t, EPI>), dim3(unsigned((threads + 255) / 256)), dim3(256),
+                     0, stream, a, L);
+  return hipGetLastError();
+}
+
+// Products with two or three weight planes always use 32 features per
+// wavefront: the 64-feature, 128-row tile would need more than the 512
+// registers of a lane.
+template <class Tr, int S, int EPI>
+static hipError_t launch_lds_shape(const GemmArgs& a, const LdsArgs& L, hipStream_t stream) {
+  if (S >= 2 || L.wave_features == 32) {
+    return L.tile_rows == 64 ? launch_lds_one<Tr, S, EPI, 32, 64>(a, L, stream)
+                             : launch_lds_one<Tr, S, EPI, 32, 128>(a, L, stream);
+  }
+  if constexpr (S == 1) {
+    return L.tile_rows == 64 ? launch_lds_one<Tr, S, EPI, 64, 64>(a, L, stream)
+                             : launch_lds_one<Tr, S, EPI, 64, 128>(a, L, stream);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_gemm_lds(const GemmArgs& a, const LdsArgs& L, GemmElem elem, int planes, GemmEpi epi,
+                           hipStream_t stream) {
+  if (a.tiles_y <= 0) return hipSuccess;
+  if (epi == EPI_SWIGLU) {
+    switch (elem) {
+      case ELEM_BF16: return launch_lds_shape<M32BF16, 2, EPI_SWIGLU>(a, L, stream);
+      case ELEM_I8: return launch_lds_shape<M32I8, 2, EPI_SWIGLU>(a, L, stream);
+      case ELEM_F32: return launch_lds_shape<M32F32, 2, EPI_SWIGLU>(a, L, stream);
+    }
+  } else {
+    switch (elem) {
+      case ELEM_BF16:
+        return planes == 3 ? launch_lds_shape<M32BF16, 3, EPI_SUM>(a, L, stream)
+                           : launch_lds_shape<M32BF16, 1, EPI_SUM>(a, L, stream);
+      case ELEM_I8: return launch_lds_shape<M32I8, 1, EPI_SUM>(a, L, stream);
+      case ELEM_F32: return launch_lds_shape<M32F32, 1, EPI_SUM>(a, L, stream);
+    }
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace moe

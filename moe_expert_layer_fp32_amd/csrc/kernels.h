@@ -46,6 +46,9 @@ struct GemmArgs {
   const float* bias;         // EPI_SUM: + bias[col] for col < n_valid
   int n_valid;
   int tiles_y;               // m-tile slots in the grid
+  int dense_tile_rows;       // dense group: rows per m-tile (16..128, multiple of 16)
+  int max_group_rows;        // grouped rows: only groups with at most this many rows (0: all)
+  int ksplit;                // streaming kernel: wavefronts sharing a column tile (1, 2 or 4)
 };
 
 hipError_t launch_gemm(const GemmArgs& a, GemmElem elem, int planes, GemmEpi epi,
@@ -54,7 +57,30 @@ hipError_t launch_gemm(const GemmArgs& a, GemmElem elem, int planes, GemmEpi epi
 // Upper bound on the m-tiles of grouped rows (R rows over G groups), and the
 // m-tiles of one dense group of `rows` rows.
 int gemm_tiles_bound(int max_rows, int n_groups);
-int gemm_tiles_dense(int rows);
+// Dense group: rows per m-tile of the streaming kernel (stored in
+// *tile_rows) and the number of m-tiles.
+int gemm_tiles_dense(int rows, int n_cols, int* tile_rows);
+// Reduction split of the streaming kernel for `col_tiles` 16-column tiles
+// (summed over groups) and a reduction of KT steps.
+int gemm_stream_ksplit(long col_tiles, int KT);
+
+// ---------------------------------------------------------------------------
+// Tiled matrix-core GEMM with LDS-staged rows (gemm_lds.hip) for groups or
+// dense problems with many rows; same GemmArgs (grouped rows / dense rows,
+// packed weights, epilogues). Requires N % (32 * wave_features / 32) == 0 and
+// K % lds_chunk_elems(elem) == 0.
+// ---------------------------------------------------------------------------
+struct LdsArgs {
+  int tile_rows;       // rows per m-tile: 64 or 128
+  int wave_features;   // output features per wavefront: 32 or 64
+  int min_rows, max_rows;   // grouped rows: groups with a row count in [min, max]
+  int splits;          // reduction split (1: epilogue in the GEMM kernel)
+  void* partial;       // splits > 1: [splits][part_rows][acc planes * N] fp32 / int32
+  int part_rows;
+};
+hipError_t launch_gemm_lds(const GemmArgs& a, const LdsArgs& L, GemmElem elem, int planes, GemmEpi epi,
+                           hipStream_t stream);
+int lds_chunk_elems(GemmElem elem);
 
 // ---------------------------------------------------------------------------
 // Gating + top-k (route.hip)
