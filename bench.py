@@ -48,6 +48,8 @@ def parse():
     p.add_argument("--layers", type=int, default=0, help="layers cycled (0: enough for > 1 GB of weights)")
     p.add_argument("--cpu-seconds", type=float, default=10.0, help="target CPU time of the oracle sample")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--streams", type=int, default=2, choices=(1, 2),
+                   help="2: the shared expert runs on a second stream (when the workload has one)")
     p.add_argument("--copy-calibration", action="store_true",
                    help="only run 5 device copies of 1 GiB (the known-size kernel for counter calibration)")
     p.add_argument("--traffic", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "CAL_FETCH_CSV", "CAL_WRITE_CSV"),
@@ -168,7 +170,7 @@ def main() -> int:
     import torch
 
     from moe_expert_layer_fp32_amd import lib as L
-    from moe_expert_layer_fp32_amd.layer import DeviceLayer
+    from moe_expert_layer_fp32_amd.layer import DeviceLayer, SecondStream
     from moe_inputs import get, make_inputs
 
     cfg = get(args.config)
@@ -203,10 +205,15 @@ def main() -> int:
         b.record()
     torch.cuda.synchronize()
     auxes = [L.MoeAux(ev_ffn1_begin=a.cuda_event, ev_ffn1_end=b.cuda_event) for a, b in ev]
+    second = SecondStream() if args.streams == 2 and cfg.shared_inter else None
+    if second is not None:
+        for a in auxes:
+            second.fill(a)
+    warm_aux = second.fill(L.MoeAux()) if second is not None else None
 
     for i in range(W):
         lay = layers[i % n_layers]
-        L.moe_layer(desc, lay.weights, lay.x, y, None, ws)
+        L.moe_layer(desc, lay.weights, lay.x, y, warm_aux, ws)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(K):
@@ -258,6 +265,7 @@ def main() -> int:
         "config": {"workload": cfg.name, "T": cfg.T, "d": cfg.d, "E": cfg.E, "k": cfg.k, "gate": cfg.gate,
                    "n_ffn": cfg.n_ffn, "n_zero": cfg.n_zero, "inter": cfg.inter,
                    "shared_inter": cfg.shared_inter, "layers_cycled": n_layers,
+                   "streams": 2 if second is not None else 1,
                    "global_batch": cfg.T, "parallelism": "none (1 GPU)"},
         "roofline": roof,
         "cpu_baseline": cpu,

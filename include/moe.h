@@ -169,6 +169,23 @@ typedef struct moe_aux {
     void* ev_ffn1_end;    /*   gate/up projection + SwiGLU kernel            */
     void* ev_ffn2_begin;  /* recorded before / after the routed-expert down  */
     void* ev_ffn2_end;    /*   projection kernel                             */
+    /* Shared-expert concurrency: when all three are given (and the layer has
+     * a shared expert), the shared FFN runs on stream2, forked from `stream`
+     * as soon as its inputs are ready and joined before the combine, so it
+     * overlaps routing and the routed experts. This is the multi-stream
+     * concurrency of gating, shared expert and feature gathering on the
+     * DeepSeek-V3/R1-on-Ascend page (Huxiu), section 模型侧并发优化, item
+     * 计算通信并发, and the two-stream overlap on page "LongCat-Flash与
+     * GLM-4.6V ...", section 破局之道：多流并行与Single-Batch Overlap.
+     * stream2 must be a non-NULL stream of the same device other than
+     * `stream`; the events are hipEvent_t created by the caller. Giving only
+     * some of the three, or stream2 equal to `stream`, is
+     * MOE_ERR_INVALID_ARG. Results are bit-identical to the single-stream
+     * call; work enqueued on `stream` after the call sees the shared expert
+     * finished. */
+    void* stream2;
+    void* ev_fork;
+    void* ev_join;
 } moe_aux;
 
 /* Workspace bytes an entry point needs for this descriptor (0 if none). */

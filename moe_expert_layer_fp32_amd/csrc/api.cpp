@@ -60,6 +60,7 @@ GemmElem router_elem(const moe_desc* d) { return d->dtype == MOE_DTYPE_F32 ? ELE
 // ---------------------------------------------------------------------------
 constexpr int PREFILL_T = 1024;
 constexpr int TARGET_WGS = 256;
+constexpr int PERSISTENT_WGS = 512;   // grid cap of the tiled kernel (it loops over tiles)
 
 struct DensePlan {
   bool lds;
@@ -90,6 +91,7 @@ DensePlan plan_dense(int M, int N, int K, GemmElem el, int nacc) {
   L.min_rows = 0;
   L.max_rows = INT32_MAX;
   L.part_rows = M;
+  L.max_wgs = PERSISTENT_WGS;
   p.tiles_y = mt;
   p.partial_bytes = splits > 1 ? size_t(splits) * M * nacc * N * 4 : 0;
   return p;
@@ -253,10 +255,12 @@ moe_status run_routed(GemmArgs g, const moe_desc* d, GemmElem el, int planes, Ge
     L.wave_features = 32;
     L.splits = 1;
     L.part_rows = r_max(d);
+    L.max_wgs = PERSISTENT_WGS;
     L.tile_rows = 64;
     L.min_rows = 1;
     L.max_rows = d->T >= PREFILL_T ? 64 : INT32_MAX;
-    g.tiles_y = ceil_div(r_max(d), L.tile_rows) + g.n_groups;
+    // with at most 64 rows an expert has one 64-row tile
+    g.tiles_y = d->T >= PREFILL_T ? g.n_groups : ceil_div(r_max(d), L.tile_rows) + g.n_groups;
     HIP_TRY(launch_gemm_lds(g, L, el, planes, epi, s));
     if (d->T >= PREFILL_T) {
       L.tile_rows = 128;
@@ -578,6 +582,11 @@ moe_status moe_layer(const moe_desc* d, const moe_weights* w, const void* x, voi
   if (st != MOE_OK) return st;
   if (!w || !w->router || !routed_weights_ok(d, w) || !shared_weights_ok(d, w)) return MOE_ERR_INVALID_ARG;
   if (d->T > 0 && (!x || !y)) return MOE_ERR_INVALID_ARG;
+  if (aux) {  // the second stream comes with both of its events, or not at all
+    const int given = !!aux->stream2 + !!aux->ev_fork + !!aux->ev_join;
+    if (given != 0 && given != 3) return MOE_ERR_INVALID_ARG;
+    if (aux->stream2 && aux->stream2 == stream) return MOE_ERR_INVALID_ARG;
+  }
   const size_t need = ws_bytes_of(d, MOE_OP_LAYER);
   if (ws_bytes < need || !ws) return MOE_ERR_WORKSPACE;
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -594,23 +603,36 @@ moe_status moe_layer(const moe_desc* d, const moe_weights* w, const void* x, voi
   if (A.q_x) L.routed.qx = L.shared.qx = A.q_x;
   if (A.s_x) L.routed.sx = L.shared.sx = A.s_x;
 
+  // The shared expert needs only x (and its int8 codes): it is forked onto
+  // the caller's second stream, when one is given, before routing starts.
+  const bool fork = d->T > 0 && d->shared_inter > 0 && A.stream2 && A.ev_fork && A.ev_join;
+  if (d->T > 0 && w8a8(d)) {
+    st = run_quant_x(d, x, L.routed, s);
+    if (st != MOE_OK) return st;
+  }
+  if (fork) {
+    hipStream_t s2 = static_cast<hipStream_t>(A.stream2);
+    HIP_TRY(hipEventRecord(static_cast<hipEvent_t>(A.ev_fork), s));
+    HIP_TRY(hipStreamWaitEvent(s2, static_cast<hipEvent_t>(A.ev_fork), 0));
+    st = run_ffn(d, shared_plan(d, w), x, L.shared, L.shared_rows, s2, nullptr, nullptr, nullptr, nullptr);
+    if (st != MOE_OK) return st;
+    HIP_TRY(hipEventRecord(static_cast<hipEvent_t>(A.ev_join), s2));
+  }
   if (d->T > 0) {
     st = run_route(d, w, x, idx, tw, L.route, s);
     if (st != MOE_OK) return st;
   }
   HIP_TRY(launch_permute(idx, d->T * d->k, d->E, counts, offsets, sorted_slot, slot_pos, s));
   if (d->T == 0) return MOE_OK;
-  if (w8a8(d)) {
-    st = run_quant_x(d, x, L.routed, s);
-    if (st != MOE_OK) return st;
-  }
   if (d->n_ffn > 0) {
     st = run_ffn(d, routed_plan(d, w, offsets, sorted_slot), x, L.routed, L.rows, s,
                  static_cast<hipEvent_t>(A.ev_ffn1_begin), static_cast<hipEvent_t>(A.ev_ffn1_end),
                  static_cast<hipEvent_t>(A.ev_ffn2_begin), static_cast<hipEvent_t>(A.ev_ffn2_end));
     if (st != MOE_OK) return st;
   }
-  if (d->shared_inter > 0) {
+  if (fork) {
+    HIP_TRY(hipStreamWaitEvent(s, static_cast<hipEvent_t>(A.ev_join), 0));
+  } else if (d->shared_inter > 0) {
     st = run_ffn(d, shared_plan(d, w), x, L.shared, L.shared_rows, s, nullptr, nullptr, nullptr, nullptr);
     if (st != MOE_OK) return st;
   }

@@ -163,6 +163,9 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int g, int row0, in
       for (int p = 0; p < D; ++p) {
         mma_stage(p);
         load_stage(p, min(kb + p + D, nst - 1));
+        // keep each refill right after its stage (the scheduler would
+        // otherwise bunch them at the end of the loop body)
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
     const int rem = nst - kb;

@@ -20,6 +20,7 @@
 // each writes raw fp32 (int32 for int8) partial sums, and gemm_reduce_kernel
 // adds them in split order and applies the epilogue, so the result does not
 // depend on scheduling.
+#include <algorithm>
 #include <type_traits>
 
 #include "common.h"
@@ -131,8 +132,28 @@ __device__ inline bool locate_tile_lds(const GemmArgs& a, int tile, int tm, int 
   return true;
 }
 
+// Number of m-tiles (rows per tile tm) among the groups whose row count lies
+// in [lo, hi]; dense: ceil(rows / tm). Wave-uniform.
+__device__ inline int count_tiles_lds(const GemmArgs& a, int tm, int lo, int hi) {
+  if (a.offsets == nullptr) return ceil_div(a.dense_rows, tm);
+  const int lane = threadIdx.x & (WAVE - 1);
+  int local = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int gg = lane * 4 + i;
+    if (gg < a.n_groups) {
+      const int n = a.offsets[a.first + gg + 1] - a.offsets[a.first + gg];
+      if (n >= lo && n <= hi) local += ceil_div(n, tm);
+    }
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) local += __shfl_xor(local, o, WAVE);
+  return local;
+}
+
 template <class Tr, int S, int EPI, int NF, int BM>
-__global__ __launch_bounds__(WG_THREADS) void gemm_lds_kernel(GemmArgs a, LdsArgs L) {
+__device__ __forceinline__ void gemm_lds_tile(const GemmArgs& a, const LdsArgs& L, uint8_t (&lds)[2][BM * LDS_ROW],
+                                              int g, int row0, int nrows, int out0, int nblock, int split) {
   constexpr int FT = NF / 32;                  // 32-feature tiles per wavefront
   constexpr int MBK = BM / 32;                 // 32-row blocks per tile
   constexpr int FB = FRAG_LANES * Tr::BPL;     // packed fragment bytes
@@ -143,26 +164,8 @@ __global__ __launch_bounds__(WG_THREADS) void gemm_lds_kernel(GemmArgs a, LdsArg
   constexpr int LOADS = BM * CH_BYTES / (WG_THREADS * 16);   // 16-byte B loads per thread per chunk
   using op_t = typename Tr::op_t;
   using acc_t = typename Tr::acc_t;
-
-  __shared__ __attribute__((aligned(16))) uint8_t lds[2][BM * LDS_ROW];
   const int lane = threadIdx.x & (WAVE - 1);
   const int wave = threadIdx.x / WAVE;
-
-  // XCD-aware linear block -> (column block, m-tile), m-tile fastest.
-  const int nbx = gridDim.x * gridDim.y;
-  const int b = blockIdx.y * gridDim.x + blockIdx.x;
-  const int q = nbx / 8;
-  const int logical = b < q * 8 ? (b % 8) * q + b / 8 : b;
-  const int tile = logical % a.tiles_y;
-  const int nblock = logical / a.tiles_y;
-  const int split = blockIdx.z;
-
-  int g, row0, nrows, out0;
-  if (!locate_tile_lds(a, tile, BM, L.min_rows, L.max_rows, g, row0, nrows, out0)) return;
-  g = __builtin_amdgcn_readfirstlane(g);
-  row0 = __builtin_amdgcn_readfirstlane(row0);
-  nrows = __builtin_amdgcn_readfirstlane(nrows);
-  out0 = __builtin_amdgcn_readfirstlane(out0);
 
   const int KT = a.K / Tr::KF;
   const int KC = a.K / CH_ELEMS;               // chunks in the whole reduction
@@ -234,16 +237,28 @@ __global__ __launch_bounds__(WG_THREADS) void gemm_lds_kernel(GemmArgs a, LdsArg
   // One chunk: matrix-core steps from LDS buffer `buf`, then the next chunk
   // (loaded two chunks ago into register stage `st`) goes to the other
   // buffer and that stage is refilled with the chunk after next.
+  auto read_b = [&](op_t (&dst)[MBK], int buf, int ks) {
+#pragma unroll
+    for (int m = 0; m < MBK; ++m)
+      dst[m] = Tr::load(&lds[buf][(m * 32 + r32) * LDS_ROW + ks * (Tr::KM * Tr::ESZ) + half * Tr::BPL]);
+  };
+  // One chunk. Inside a step: read the next step's LDS operands, run this
+  // step's matrix-core work, refill this step's weight slot RA steps ahead;
+  // scheduling barriers keep that order (left alone, the compiler sinks the
+  // refills to the end of the chunk, which empties the weight ring). After
+  // the chunk the next chunk (loaded two chunks ago into register stage
+  // `st`) goes to the other LDS buffer and the stage is refilled.
   auto chunk = [&](auto st_tag, int c) {
     constexpr int st = decltype(st_tag)::value;
     const int buf = c & 1;
+    op_t bfa[MBK], bfb[MBK];
+    read_b(bfa, buf, 0);
 #pragma unroll
     for (int ks = 0; ks < CH_KS; ++ks) {
       const int slot = ks % RA;
-      op_t bf[MBK];
-#pragma unroll
-      for (int m = 0; m < MBK; ++m)
-        bf[m] = Tr::load(&lds[buf][(m * 32 + r32) * LDS_ROW + ks * (Tr::KM * Tr::ESZ) + half * Tr::BPL]);
+      op_t(&cur)[MBK] = (ks & 1) ? bfb : bfa;
+      op_t(&nxt)[MBK] = (ks & 1) ? bfa : bfb;
+      if (ks + 1 < CH_KS) read_b(nxt, buf, ks + 1);
 #pragma unroll
       for (int f = 0; f < FT; ++f)
 #pragma unroll
@@ -251,9 +266,10 @@ __global__ __launch_bounds__(WG_THREADS) void gemm_lds_kernel(GemmArgs a, LdsArg
 #pragma unroll
           for (int m = 0; m < MBK; ++m) {
             const int sa = (EPI == EPI_SWIGLU) ? s : 0;
-            acc[sa][f][m] = Tr::mfma(aring[slot][f][s], bf[m], acc[sa][f][m]);
+            acc[sa][f][m] = Tr::mfma(aring[slot][f][s], cur[m], acc[sa][f][m]);
           }
       load_a(slot, min(c * CH_KS + ks + RA, nsteps - 1));
+      __builtin_amdgcn_sched_barrier(0);
     }
     store_b(st, buf ^ 1);          // chunk c + 1 (a copy nobody reads after the last)
     load_b(st, min(c + 3, nch - 1));
@@ -336,6 +352,37 @@ __global__ __launch_bounds__(WG_THREADS) void gemm_lds_kernel(GemmArgs a, LdsArg
   }
 }
 
+// Persistent over tiles: the grid is a fixed number of workgroups (a
+// multiple of 8); the tiles (column block x m-tile, m-tile fastest) are
+// counted on the device from the offsets, cut into 8 contiguous ranges, one
+// per XCD (blocks are dealt to the XCDs round-robin, so block b runs on XCD
+// b % 8), and each workgroup walks its XCD's range with a stride of the
+// workgroups on that XCD. Tiles sharing a weight column block thus run close
+// together in time on one L2.
+template <class Tr, int S, int EPI, int NF, int BM>
+__global__ __launch_bounds__(WG_THREADS) __attribute__((amdgpu_waves_per_eu(BM == 64 && NF == 32 ? 2 : 1)))
+void gemm_lds_kernel(GemmArgs a, LdsArgs L) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds[2][BM * LDS_ROW];
+  const int tiles = count_tiles_lds(a, BM, L.min_rows, L.max_rows);
+  const int nblocks = ceil_div(a.N, WG_WAVES * NF);
+  const int total = tiles * nblocks;
+  const int nwg = gridDim.x;
+  const int xcd = blockIdx.x % 8, slot = blockIdx.x / 8, per_xcd_wg = nwg / 8;
+  const int q = ceil_div(total, 8);
+  const int lo = xcd * q, hi = min(total, lo + q);
+  for (int logical = lo + slot; logical < hi; logical += per_xcd_wg) {
+    const int tile = logical % tiles;
+    const int nblock = logical / tiles;
+    int g, row0, nrows, out0;
+    if (!locate_tile_lds(a, tile, BM, L.min_rows, L.max_rows, g, row0, nrows, out0)) break;
+    g = __builtin_amdgcn_readfirstlane(g);
+    row0 = __builtin_amdgcn_readfirstlane(row0);
+    nrows = __builtin_amdgcn_readfirstlane(nrows);
+    out0 = __builtin_amdgcn_readfirstlane(out0);
+    gemm_lds_tile<Tr, S, EPI, NF, BM>(a, L, lds, g, row0, nrows, out0, nblock, blockIdx.z);
+  }
+}
+
 // Sum of the split partials in split order, then the epilogue of the
 // product. One thread per 4 output columns of one row; rows of the selected
 // groups only.
@@ -406,7 +453,10 @@ int lds_chunk_elems(GemmElem elem) { return CH_BYTES / (elem == ELEM_F32 ? 4 : (
 
 template <class Tr, int S, int EPI, int NF, int BM>
 static hipError_t launch_lds_one(const GemmArgs& a, const LdsArgs& L, hipStream_t stream) {
-  const dim3 grid(ceil_div(a.N, WG_WAVES * NF), a.tiles_y, L.splits);
+  // persistent grid: at most `tiles_y` m-tiles per column block exist
+  const long bound = long(ceil_div(a.N, WG_WAVES * NF)) * a.tiles_y;
+  const int nwg = int(std::max(8L, std::min(bound, long(L.max_wgs)) / 8 * 8));
+  const dim3 grid(nwg, 1, L.splits);
   hipLaunchKernelGGL((gemm_lds_kernel<Tr, S, EPI, NF, BM>), grid, dim3(WG_THREADS), 0, stream, a, L);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || L.splits == 1) return e;

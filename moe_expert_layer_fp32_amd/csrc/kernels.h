@@ -77,6 +77,7 @@ struct LdsArgs {
   int splits;          // reduction split (1: epilogue in the GEMM kernel)
   void* partial;       // splits > 1: [splits][part_rows][acc planes * N] fp32 / int32
   int part_rows;
+  int max_wgs;         // cap of the persistent grid (workgroups per split)
 };
 hipError_t launch_gemm_lds(const GemmArgs& a, const LdsArgs& L, GemmElem elem, int planes, GemmEpi epi,
                            hipStream_t stream);

@@ -26,6 +26,29 @@ def empty_bytes(n: int, device="cuda") -> torch.Tensor:
     return torch.empty(max(int(n), 1), dtype=torch.uint8, device=device)
 
 
+def event_handle(ev: torch.cuda.Event) -> int:
+    """The hipEvent_t behind a torch event (torch creates it on first record)."""
+    if ev.cuda_event == 0:
+        ev.record()
+    return ev.cuda_event
+
+
+class SecondStream:
+    """A second stream of default priority with the fork/join events that
+    moe_aux takes for running the shared expert concurrently."""
+
+    def __init__(self, device="cuda"):
+        self.stream = torch.cuda.Stream(device=device)
+        self.fork = torch.cuda.Event()
+        self.join = torch.cuda.Event()
+
+    def fill(self, aux: L.MoeAux) -> L.MoeAux:
+        aux.stream2 = self.stream.cuda_stream
+        aux.ev_fork = event_handle(self.fork)
+        aux.ev_join = event_handle(self.join)
+        return aux
+
+
 class DeviceLayer:
     """Packed weights of one layer plus convenience wrappers of the C ABI."""
 
@@ -123,11 +146,14 @@ class DeviceLayer:
         L.moe_combine(self.desc_for(T), x, rows, shared_rows, topk_idx, topk_w, offsets, slot_pos, y)
         return y
 
-    def layer(self, x=None, y=None, aux: L.MoeAux | None = None, ws=None):
+    def layer(self, x=None, y=None, aux: L.MoeAux | None = None, ws=None, second: SecondStream | None = None):
+        """moe_layer; with `second`, the shared expert runs on its stream."""
         x = self.x if x is None else x
         T = x.shape[0]
         y = torch.empty((T, self.cfg.d), dtype=self.xdtype, device=self.device) if y is None else y
         ws = self.workspace(L.OP_LAYER, T) if ws is None else ws
+        if second is not None:
+            aux = second.fill(L.MoeAux() if aux is None else aux)
         L.moe_layer(self.desc_for(T), self.weights, x, y, aux, ws)
         return y
 

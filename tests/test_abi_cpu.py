@@ -39,10 +39,10 @@ def test_library_exports_every_declared_function(L):
 
 
 def test_struct_sizes_match_header(L):
-    # 16 int32 + 1 float; 12 pointers; 12 pointers
+    # 16 int32 + 1 float; 12 pointers; 15 pointers
     assert ctypes.sizeof(L.MoeDesc) == 17 * 4
     assert ctypes.sizeof(L.MoeWeights) == 12 * 8
-    assert ctypes.sizeof(L.MoeAux) == 12 * 8
+    assert ctypes.sizeof(L.MoeAux) == 15 * 8
 
 
 def test_status_strings(L):
@@ -125,6 +125,21 @@ def test_workspace_too_small_and_null_pointers(L):
     assert lib.moe_grouped_ffn(ctypes.byref(d), ctypes.byref(w), 5, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 40,
                                None) == -1
     assert lib.moe_route_topk(ctypes.byref(d), ctypes.byref(w), FAKE, FAKE, FAKE, FAKE, 1 << 40, None) == -1
+
+
+def test_second_stream_needs_both_events(L):
+    d = _desc(L)
+    lib = L.load_library()
+    w = L.MoeWeights(router=FAKE, w13=FAKE, w2=FAKE, sw13=FAKE, sw2=FAKE)
+    for given in (dict(stream2=FAKE), dict(stream2=FAKE, ev_fork=FAKE), dict(ev_join=FAKE),
+                  dict(stream2=FAKE, ev_fork=FAKE, ev_join=FAKE, stream=FAKE)):
+        stream = given.pop("stream", None)
+        aux = L.MoeAux(**given)
+        assert lib.moe_layer(ctypes.byref(d), ctypes.byref(w), FAKE, FAKE, ctypes.byref(aux), FAKE, 1 << 40,
+                             stream) == -1, given
+    # all three given: validation passes and only the workspace check fails
+    aux = L.MoeAux(stream2=FAKE, ev_fork=FAKE, ev_join=FAKE)
+    assert lib.moe_layer(ctypes.byref(d), ctypes.byref(w), FAKE, FAKE, ctypes.byref(aux), FAKE, 0, None) == -3
 
 
 def test_pack_rejects_small_destination(L):

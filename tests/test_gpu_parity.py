@@ -381,6 +381,26 @@ def test_layer_prefill_sampled_tokens():
     _check_layer(cfg, inp, lay, tokens=np.sort(toks))
 
 
+def _bits(t):
+    return t.view(torch.int16) if t.dtype == torch.bfloat16 else t
+
+
+@pytest.mark.parametrize("name,T", [("prefill_zipf_bf16", None), ("dsv3_decode_share_bf16", None),
+                                    ("dsv3_decode_share_bf16", 129), ("pangu_moge_w8a8", None)])
+def test_layer_shared_expert_on_second_stream(name, T):
+    """The shared expert forked onto a second stream gives the single-stream
+    result bit for bit, and the caller's stream sees it joined."""
+    from moe_expert_layer_fp32_amd.layer import SecondStream
+    lay = U.device_layer(name, T)
+    U.say(f"[gpu] second stream {name} T={lay.cfg.T}")
+    one = lay.layer().clone()
+    second = SecondStream()
+    for _ in range(3):
+        two = lay.layer(second=second).clone()     # consumed on the caller's stream, no host sync between
+        torch.cuda.synchronize()
+        assert torch.equal(_bits(one), _bits(two))
+
+
 @pytest.mark.parametrize("name", ["longcat_zero_bf16", "dsv3_decode_share_bf16", "pangu_moge_w8a8"])
 def test_layer_is_deterministic(name):
     cfg, inp = U.inputs(name)
