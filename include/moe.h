@@ -153,8 +153,8 @@ typedef struct moe_weights {
 /*
  * Optional outputs and hooks of moe_layer; any NULL member is skipped. The
  * table members, when given, are written instead of workspace copies (same
- * contents as moe_route_topk / moe_permute produce). The events (hipEvent_t)
- * are recorded on `stream` around the stages of the layer, for timing.
+ * contents as moe_route_topk / moe_permute produce). The events are
+ * hipEvent_t of the caller, used for timing.
  */
 typedef struct moe_aux {
     int32_t* topk_idx;    /* [T][k] */
@@ -165,10 +165,14 @@ typedef struct moe_aux {
     int32_t* slot_pos;    /* [T*k] */
     int8_t* q_x;          /* W8A8: [T][d] per-token int8 codes of x */
     float* s_x;           /* W8A8: [T] their scales */
-    void* ev_ffn1_begin;  /* recorded before / after the routed-expert       */
-    void* ev_ffn1_end;    /*   gate/up projection + SwiGLU kernel            */
-    void* ev_ffn2_begin;  /* recorded before / after the routed-expert down  */
-    void* ev_ffn2_end;    /*   projection kernel                             */
+    /* Timing events, stamped by the runtime when the routed-expert kernels
+     * start and end (hipExtLaunchKernel), so the elapsed time between a
+     * begin/end pair is those kernels' own duration, with no marker packet
+     * between kernels. Create them with timing enabled. */
+    void* ev_ffn1_begin;  /* start / end of the routed-expert gate/up      */
+    void* ev_ffn1_end;    /*   projection + SwiGLU (first to last kernel)  */
+    void* ev_ffn2_begin;  /* start / end of the routed-expert down         */
+    void* ev_ffn2_end;    /*   projection (first to last kernel)           */
     /* Shared-expert concurrency: when all three are given (and the layer has
      * a shared expert), the shared FFN runs on stream2, forked from `stream`
      * as soon as its inputs are ready and joined before the combine, so it

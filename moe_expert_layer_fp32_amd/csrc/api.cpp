@@ -224,7 +224,8 @@ LayerWs carve_layer(Carve& c, const moe_desc* d) {
 // stages
 // ---------------------------------------------------------------------------
 // Launch one dense product with its plan (tiled LDS GEMM or streaming).
-moe_status run_dense(GemmArgs g, int M, GemmElem el, int planes, GemmEpi epi, void* partial, hipStream_t s) {
+moe_status run_dense(GemmArgs g, int M, GemmElem el, int planes, GemmEpi epi, void* partial, hipStream_t s,
+                     KernelEvents ev = {}) {
   const DensePlan p = plan_dense(M, g.N, g.K, el, epi == EPI_SWIGLU ? 2 : 1);
   g.offsets = nullptr;
   g.dense_rows = M;
@@ -232,12 +233,12 @@ moe_status run_dense(GemmArgs g, int M, GemmElem el, int planes, GemmEpi epi, vo
   if (!p.lds) {
     g.dense_tile_rows = p.tile_rows;
     g.ksplit = gemm_stream_ksplit(g.N / 16, g.K / kf_of(el));
-    HIP_TRY(launch_gemm(g, el, planes, epi, s));
+    HIP_TRY(launch_gemm(g, el, planes, epi, s, ev));
     return MOE_OK;
   }
   LdsArgs L = p.L;
   L.partial = partial;
-  HIP_TRY(launch_gemm_lds(g, L, el, planes, epi, s));
+  HIP_TRY(launch_gemm_lds(g, L, el, planes, epi, s, ev));
   return MOE_OK;
 }
 
@@ -248,7 +249,8 @@ moe_status run_dense(GemmArgs g, int M, GemmElem el, int planes, GemmEpi epi, vo
 // more rows). Few experts with long rows (fewer than TARGET_WGS tiled
 // workgroups, e.g. 8 resident experts of d 7168) and shapes that do not tile
 // stream through gemm_rows_kernel, whose wavefronts split the reduction.
-moe_status run_routed(GemmArgs g, const moe_desc* d, GemmElem el, int planes, GemmEpi epi, hipStream_t s) {
+moe_status run_routed(GemmArgs g, const moe_desc* d, GemmElem el, int planes, GemmEpi epi, hipStream_t s,
+                      KernelEvents ev = {}) {
   const long tiled_wgs = long(g.n_groups) * ceil_div(g.N, 128);
   if (routed_tiled(d, g.N, g.K) && (tiled_wgs >= TARGET_WGS || d->T >= PREFILL_T)) {
     LdsArgs L{};
@@ -261,27 +263,53 @@ moe_status run_routed(GemmArgs g, const moe_desc* d, GemmElem el, int planes, Ge
     L.max_rows = d->T >= PREFILL_T ? 64 : INT32_MAX;
     // with at most 64 rows an expert has one 64-row tile
     g.tiles_y = d->T >= PREFILL_T ? g.n_groups : ceil_div(r_max(d), L.tile_rows) + g.n_groups;
-    HIP_TRY(launch_gemm_lds(g, L, el, planes, epi, s));
-    if (d->T >= PREFILL_T) {
-      L.tile_rows = 128;
-      L.min_rows = 65;
-      L.max_rows = INT32_MAX;
-      g.tiles_y = ceil_div(r_max(d), L.tile_rows) + g.n_groups;
-      HIP_TRY(launch_gemm_lds(g, L, el, planes, epi, s));
+    if (d->T < PREFILL_T) {
+      HIP_TRY(launch_gemm_lds(g, L, el, planes, epi, s, ev));
+      return MOE_OK;
     }
+    HIP_TRY(launch_gemm_lds(g, L, el, planes, epi, s, KernelEvents{ev.start, nullptr}));
+    L.tile_rows = 128;
+    L.min_rows = 65;
+    L.max_rows = INT32_MAX;
+    g.tiles_y = ceil_div(r_max(d), L.tile_rows) + g.n_groups;
+    HIP_TRY(launch_gemm_lds(g, L, el, planes, epi, s, KernelEvents{nullptr, ev.stop}));
     return MOE_OK;
   }
   g.max_group_rows = 0;
   g.tiles_y = gemm_tiles_bound(r_max(d), g.n_groups);
   g.ksplit = gemm_stream_ksplit(long(g.n_groups) * (g.N / 16), g.K / kf_of(el));
-  HIP_TRY(launch_gemm(g, el, planes, epi, s));
+  HIP_TRY(launch_gemm(g, el, planes, epi, s, ev));
   return MOE_OK;
+}
+
+// Router products small enough that every 16-token block may read the whole
+// packed router (at most ROUTER_SMALL_BYTES of router reads in all, at most
+// ROUTER_WG_BYTES per workgroup of 16 experts) go to the one-pass router
+// kernel; larger ones to the GEMM kernels, whose split-K partial sums the
+// gate kernel adds itself (no reduce pass).
+constexpr size_t ROUTER_SMALL_BYTES = size_t(32) << 20;
+constexpr size_t ROUTER_WG_BYTES = size_t(256) << 10;
+
+bool router_small(const moe_desc* d) {
+  const size_t per_k = d->dtype == MOE_DTYPE_F32 ? 4 : 6;   // one fp32 or three bf16 planes
+  const size_t router_bytes = size_t(e_pad(d)) * d->d * per_k;
+  return size_t(16) * d->d * per_k <= ROUTER_WG_BYTES &&
+         size_t(ceil_div(d->T, 16)) * router_bytes <= ROUTER_SMALL_BYTES;
 }
 
 moe_status run_route(const moe_desc* d, const moe_weights* w, const void* x, int32_t* idx, float* tw,
                      const RouteWs& ws, hipStream_t s) {
-  GemmArgs g{};
   const bool f32 = d->dtype == MOE_DTYPE_F32;
+  GateArgs ga{ws.z, e_pad(d), d->T, d->E, d->k, d->gate, d->n_group, d->topk_group, d->per_group_k,
+              d->renorm, d->route_scale, idx, tw, nullptr, 0, nullptr};
+  if (router_small(d)) {
+    const RouterArgs ra{static_cast<const uint8_t*>(w->router), static_cast<const uint8_t*>(x), d->T, d->d, d->E,
+                        e_pad(d), w->logit_bias, ws.z};
+    HIP_TRY(launch_router_small(ra, f32, s));
+    HIP_TRY(launch_gate(ga, s));
+    return MOE_OK;
+  }
+  GemmArgs g{};
   g.A = static_cast<const uint8_t*>(w->router);
   g.a_group_stride = 0;
   g.K = d->d;
@@ -294,10 +322,25 @@ moe_status run_route(const moe_desc* d, const moe_weights* w, const void* x, int
   g.out_bf16 = 0;
   g.bias = w->logit_bias;
   g.n_valid = d->E;
-  moe_status st = run_dense(g, d->T, f32 ? ELEM_F32 : ELEM_BF16, f32 ? 1 : 3, EPI_SUM, ws.partial, s);
-  if (st != MOE_OK) return st;
-  GateArgs ga{ws.z, e_pad(d), d->T, d->E, d->k, d->gate, d->n_group, d->topk_group, d->per_group_k,
-              d->renorm, d->route_scale, idx, tw};
+  const GemmElem el = f32 ? ELEM_F32 : ELEM_BF16;
+  const DensePlan p = plan_dense(d->T, g.N, g.K, el, 1);
+  g.offsets = nullptr;
+  g.tiles_y = p.tiles_y;
+  if (!p.lds) {
+    g.dense_tile_rows = p.tile_rows;
+    g.ksplit = gemm_stream_ksplit(g.N / 16, g.K / kf_of(el));
+    HIP_TRY(launch_gemm(g, el, f32 ? 1 : 3, EPI_SUM, s));
+  } else {
+    LdsArgs L = p.L;
+    L.partial = ws.partial;
+    L.fold_reduce = 1;
+    HIP_TRY(launch_gemm_lds(g, L, el, f32 ? 1 : 3, EPI_SUM, s));
+    if (L.splits > 1) {
+      ga.partial = static_cast<const float*>(ws.partial);
+      ga.splits = L.splits;
+      ga.bias = w->logit_bias;
+    }
+  }
   HIP_TRY(launch_gate(ga, s));
   return MOE_OK;
 }
@@ -345,10 +388,10 @@ moe_status run_ffn(const moe_desc* d, const FfnPlan& p, const void* x, const Ffn
   g1.out = f.h;
   g1.ldo = size_t(p.inter) * h_bytes(d);
   g1.out_bf16 = d->dtype == MOE_DTYPE_BF16;
-  if (e1b) HIP_TRY(hipEventRecord(e1b, s));
-  st = routed ? run_routed(g1, d, el, 2, EPI_SWIGLU, s) : run_dense(g1, d->T, el, 2, EPI_SWIGLU, f.partial, s);
+  const KernelEvents ev1{e1b, e1e}, ev2{e2b, e2e};
+  st = routed ? run_routed(g1, d, el, 2, EPI_SWIGLU, s, ev1)
+              : run_dense(g1, d->T, el, 2, EPI_SWIGLU, f.partial, s, ev1);
   if (st != MOE_OK) return st;
-  if (e1e) HIP_TRY(hipEventRecord(e1e, s));
 
   if (w8a8(d)) {
     HIP_TRY(launch_quant_rows(f.h, 0, p.inter, p.rows_bound, p.offsets, p.first, p.groups, f.qh, f.sh, s));
@@ -372,10 +415,9 @@ moe_status run_ffn(const moe_desc* d, const FfnPlan& p, const void* x, const Ffn
   g2.out = reinterpret_cast<uint8_t*>(rows);
   g2.ldo = size_t(d->d) * 4;
   g2.out_bf16 = 0;
-  if (e2b) HIP_TRY(hipEventRecord(e2b, s));
-  st = routed ? run_routed(g2, d, el, 1, EPI_SUM, s) : run_dense(g2, d->T, el, 1, EPI_SUM, f.partial, s);
+  st = routed ? run_routed(g2, d, el, 1, EPI_SUM, s, ev2)
+              : run_dense(g2, d->T, el, 1, EPI_SUM, f.partial, s, ev2);
   if (st != MOE_OK) return st;
-  if (e2e) HIP_TRY(hipEventRecord(e2e, s));
   return MOE_OK;
 }
 

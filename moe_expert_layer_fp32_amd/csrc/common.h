@@ -1,6 +1,7 @@
 // Device-side types and helpers shared by the gfx950 kernels of libmoe.so.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
@@ -26,6 +27,26 @@ constexpr int WG_THREADS = WG_WAVES * WAVE;
 constexpr int WG_N = WG_WAVES * TILE_N;             // 64 output columns per workgroup
 
 __host__ __device__ inline int ceil_div(int a, int b) { return (a + b - 1) / b; }
+
+// Launch with optional start / stop timing events stamped by the kernel's
+// own dispatch (no event is recorded when both are null).
+template <typename K, typename... Args>
+inline hipError_t launch_timed(K kernel, dim3 grid, dim3 block, hipStream_t s, hipEvent_t start, hipEvent_t stop,
+                               Args... args) {
+  if (start || stop)
+    hipExtLaunchKernelGGL(kernel, grid, block, 0, s, start, stop, 0, args...);
+  else
+    hipLaunchKernelGGL(kernel, grid, block, 0, s, args...);
+  return hipGetLastError();
+}
+// A launcher that launches nothing still records its events (in order).
+inline hipError_t record_events(hipEvent_t start, hipEvent_t stop, hipStream_t s) {
+  if (start) {
+    const hipError_t e = hipEventRecord(start, s);
+    if (e != hipSuccess) return e;
+  }
+  return stop ? hipEventRecord(stop, s) : hipSuccess;
+}
 
 // ---------------------------------------------------------------------------
 // bf16 helpers
@@ -98,24 +119,54 @@ __host__ __device__ constexpr int frag_bytes() { return FRAG_LANES * Tr::BPL; }
 
 // ---------------------------------------------------------------------------
 // wavefront reductions
+//
+// Data-parallel-primitive moves inside each row of 16 lanes: after a quad
+// swap of neighbours, a quad swap of pairs, the half-row mirror and the row
+// mirror, every lane holds the combination of its whole row (the operation
+// must be commutative: partner lanes then compute identical values). The
+// four row results are read into scalar registers and combined in lane
+// order, so every lane gets the same value and the order never varies.
 // ---------------------------------------------------------------------------
-__device__ inline float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, WAVE));
+constexpr int DPP_QUAD_1032 = 0xB1;        // quad_perm [1,0,3,2]
+constexpr int DPP_QUAD_2301 = 0x4E;        // quad_perm [2,3,0,1]
+constexpr int DPP_ROW_HALF_MIRROR = 0x141;
+constexpr int DPP_ROW_MIRROR = 0x140;
+
+template <int CTRL>
+__device__ inline uint32_t dpp_u32(uint32_t v) {
+  return uint32_t(__builtin_amdgcn_update_dpp(0, int(v), CTRL, 0xF, 0xF, false));
+}
+template <int CTRL>
+__device__ inline float dpp_f32(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+__device__ inline uint32_t lane_u32(uint32_t v, int l) { return uint32_t(__builtin_amdgcn_readlane(int(v), l)); }
+__device__ inline float lane_f32(float v, int l) { return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l)); }
+
+template <class Op>
+__device__ inline float row_reduce_f32(float v, Op op) {
+  v = op(v, dpp_f32<DPP_QUAD_1032>(v));
+  v = op(v, dpp_f32<DPP_QUAD_2301>(v));
+  v = op(v, dpp_f32<DPP_ROW_HALF_MIRROR>(v));
+  v = op(v, dpp_f32<DPP_ROW_MIRROR>(v));
   return v;
+}
+
+// All 64 lanes of the wavefront must be active.
+__device__ inline float wave_max(float v) {
+  v = row_reduce_f32(v, [](float a, float b) { return fmaxf(a, b); });
+  return fmaxf(fmaxf(lane_f32(v, 0), lane_f32(v, 16)), fmaxf(lane_f32(v, 32), lane_f32(v, 48)));
 }
 __device__ inline float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, WAVE);
-  return v;
+  v = row_reduce_f32(v, [](float a, float b) { return a + b; });
+  return (lane_f32(v, 0) + lane_f32(v, 16)) + (lane_f32(v, 32) + lane_f32(v, 48));
 }
-__device__ inline uint64_t wave_max_u64(uint64_t v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    uint64_t w = __shfl_xor(v, o, WAVE);
-    v = w > v ? w : v;
-  }
-  return v;
+__device__ inline uint32_t wave_max_u32(uint32_t v) {
+  v = max(v, dpp_u32<DPP_QUAD_1032>(v));
+  v = max(v, dpp_u32<DPP_QUAD_2301>(v));
+  v = max(v, dpp_u32<DPP_ROW_HALF_MIRROR>(v));
+  v = max(v, dpp_u32<DPP_ROW_MIRROR>(v));
+  return max(max(lane_u32(v, 0), lane_u32(v, 16)), max(lane_u32(v, 32), lane_u32(v, 48)));
 }
 
 }  // namespace moe

@@ -287,29 +287,28 @@ int gemm_tiles_dense(int rows, int n_cols, int* tile_rows) {
 }
 
 template <class Tr, int S, int EPI>
-static hipError_t launch_one(const GemmArgs& a, hipStream_t stream) {
-  if (a.tiles_y <= 0) return hipSuccess;
+static hipError_t launch_one(const GemmArgs& a, hipStream_t stream, KernelEvents ev) {
+  if (a.tiles_y <= 0) return record_events(ev.start, ev.stop, stream);
   const int wn = WG_WAVES / a.ksplit;
   dim3 grid(ceil_div(a.N, wn * TILE_N), a.tiles_y);   // linearised and remapped in the kernel
-  hipLaunchKernelGGL((gemm_rows_kernel<Tr, S, EPI>), grid, dim3(WG_THREADS), 0, stream, a);
-  return hipGetLastError();
+  return launch_timed((gemm_rows_kernel<Tr, S, EPI>), grid, dim3(WG_THREADS), stream, ev.start, ev.stop, a);
 }
 
 hipError_t launch_gemm(const GemmArgs& a, GemmElem elem, int planes, GemmEpi epi,
-                       hipStream_t stream) {
+                       hipStream_t stream, KernelEvents ev) {
   if (epi == EPI_SWIGLU) {
     switch (elem) {
-      case ELEM_BF16: return launch_one<TrBF16, 2, EPI_SWIGLU>(a, stream);
-      case ELEM_I8: return launch_one<TrI8, 2, EPI_SWIGLU>(a, stream);
-      case ELEM_F32: return launch_one<TrF32, 2, EPI_SWIGLU>(a, stream);
+      case ELEM_BF16: return launch_one<TrBF16, 2, EPI_SWIGLU>(a, stream, ev);
+      case ELEM_I8: return launch_one<TrI8, 2, EPI_SWIGLU>(a, stream, ev);
+      case ELEM_F32: return launch_one<TrF32, 2, EPI_SWIGLU>(a, stream, ev);
     }
   } else {
     switch (elem) {
       case ELEM_BF16:
-        return planes == 3 ? launch_one<TrBF16, 3, EPI_SUM>(a, stream)
-                           : launch_one<TrBF16, 1, EPI_SUM>(a, stream);
-      case ELEM_I8: return launch_one<TrI8, 1, EPI_SUM>(a, stream);
-      case ELEM_F32: return launch_one<TrF32, 1, EPI_SUM>(a, stream);
+        return planes == 3 ? launch_one<TrBF16, 3, EPI_SUM>(a, stream, ev)
+                           : launch_one<TrBF16, 1, EPI_SUM>(a, stream, ev);
+      case ELEM_I8: return launch_one<TrI8, 1, EPI_SUM>(a, stream, ev);
+      case ELEM_F32: return launch_one<TrF32, 1, EPI_SUM>(a, stream, ev);
     }
   }
   return hipErrorInvalidValue;

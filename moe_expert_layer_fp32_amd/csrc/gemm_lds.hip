@@ -151,7 +151,7 @@ __device__ inline int count_tiles_lds(const GemmArgs& a, int tm, int lo, int hi)
   return local;
 }
 
-template <class Tr, int S, int EPI, int NF, int BM>
+template <class Tr, int S, int EPI, int NF, int BM, int RA>
 __device__ __forceinline__ void gemm_lds_tile(const GemmArgs& a, const LdsArgs& L, uint8_t (&lds)[2][BM * LDS_ROW],
                                               int g, int row0, int nrows, int out0, int nblock, int split) {
   constexpr int FT = NF / 32;                  // 32-feature tiles per wavefront
@@ -172,6 +172,33 @@ __device__ __forceinline__ void gemm_lds_tile(const GemmArgs& a, const LdsArgs& 
   const int c_begin = split * KC / L.splits;
   const int c_end = (split + 1) * KC / L.splits;
   const int nch = c_end - c_begin;
+
+  // ---- A: this wavefront's feature tiles, straight from global ----
+  // A wavefront past the last feature tile (N not a multiple of the block)
+  // computes a copy of the last tile and stores nothing.
+  const int ft_first = (nblock * WG_WAVES + wave) * FT;
+  const bool wave_live = ft_first * 32 < a.N;
+  const int ft0 = wave_live ? ft_first : a.N / 32 - FT;
+  const int r32 = lane & 31, half = lane >> 5;
+  const uint8_t* abase = a.A + size_t(g) * a.a_group_stride +
+                         size_t((2 * ft0 + (r32 >> 4)) * KT) * S * FB + (half * 16 + (r32 & 15)) * Tr::BPL;
+  // Ring of RA matrix-core steps of weight operands, refilled RA steps ahead
+  // across chunk boundaries. Every load is unconditional (steps past the end
+  // re-read the last one), so the waits only drain the step being used.
+  static_assert((2 * CH_KS) % RA == 0, "ring must divide two chunks");
+  op_t aring[RA][FT][S];
+  const int nsteps = nch * CH_KS;
+  auto load_a = [&](int slot, int i) {
+    const int kt = c_begin * CH_KT + (i >> 1);
+    const int h = i & 1;
+#pragma unroll
+    for (int f = 0; f < FT; ++f)
+#pragma unroll
+      for (int s = 0; s < S; ++s)
+        aring[slot][f][s] =
+            Tr::load(abase + (size_t(2 * f) * KT * S + size_t(kt) * S + s) * FB + h * 2 * 16 * Tr::BPL);
+  };
+
 
   // ---- B staging: this thread's rows and byte column inside a chunk ----
   const uint8_t* bsrc[LOADS];
@@ -195,33 +222,6 @@ __device__ __forceinline__ void gemm_lds_tile(const GemmArgs& a, const LdsArgs& 
   auto store_b = [&](int st, int buf) {
 #pragma unroll
     for (int i = 0; i < LOADS; ++i) *reinterpret_cast<u32x4*>(&lds[buf][bdst[i]]) = bstage[st][i];
-  };
-
-  // ---- A: this wavefront's feature tiles, straight from global ----
-  // A wavefront past the last feature tile (N not a multiple of the block)
-  // computes a copy of the last tile and stores nothing.
-  const int ft_first = (nblock * WG_WAVES + wave) * FT;
-  const bool wave_live = ft_first * 32 < a.N;
-  const int ft0 = wave_live ? ft_first : a.N / 32 - FT;
-  const int r32 = lane & 31, half = lane >> 5;
-  const uint8_t* abase = a.A + size_t(g) * a.a_group_stride +
-                         size_t((2 * ft0 + (r32 >> 4)) * KT) * S * FB + (half * 16 + (r32 & 15)) * Tr::BPL;
-  // Ring of RA matrix-core steps of weight operands, refilled RA steps ahead
-  // across chunk boundaries. Every load is unconditional (steps past the end
-  // re-read the last one), so the waits only drain the step being used.
-  constexpr int RA = 8;
-  static_assert(CH_KS % RA == 0, "ring must divide the chunk");
-  op_t aring[RA][FT][S];
-  const int nsteps = nch * CH_KS;
-  auto load_a = [&](int slot, int i) {
-    const int kt = c_begin * CH_KT + (i >> 1);
-    const int h = i & 1;
-#pragma unroll
-    for (int f = 0; f < FT; ++f)
-#pragma unroll
-      for (int s = 0; s < S; ++s)
-        aring[slot][f][s] =
-            Tr::load(abase + (size_t(2 * f) * KT * S + size_t(kt) * S + s) * FB + h * 2 * 16 * Tr::BPL);
   };
 
   acc_t acc[NACC][FT][MBK];
@@ -255,7 +255,7 @@ __device__ __forceinline__ void gemm_lds_tile(const GemmArgs& a, const LdsArgs& 
     read_b(bfa, buf, 0);
 #pragma unroll
     for (int ks = 0; ks < CH_KS; ++ks) {
-      const int slot = ks % RA;
+      const int slot = ((st ^ 1) * CH_KS + ks) % RA;   // chunk c has parity st ^ 1
       op_t(&cur)[MBK] = (ks & 1) ? bfb : bfa;
       op_t(&nxt)[MBK] = (ks & 1) ? bfa : bfb;
       if (ks + 1 < CH_KS) read_b(nxt, buf, ks + 1);
@@ -360,7 +360,12 @@ __device__ __forceinline__ void gemm_lds_tile(const GemmArgs& a, const LdsArgs& 
 // workgroups on that XCD. Tiles sharing a weight column block thus run close
 // together in time on one L2.
 template <class Tr, int S, int EPI, int NF, int BM>
-__global__ __launch_bounds__(WG_THREADS) __attribute__((amdgpu_waves_per_eu(BM == 64 && NF == 32 ? 2 : 1)))
+constexpr int ring_steps() { return 8; }
+template <class Tr, int S, int EPI, int NF, int BM>
+constexpr int lds_waves_per_eu() { return BM == 64 && NF == 32 && ring_steps<Tr, S, EPI, NF, BM>() == 8 ? 2 : 1; }
+
+template <class Tr, int S, int EPI, int NF, int BM>
+__global__ __launch_bounds__(WG_THREADS) __attribute__((amdgpu_waves_per_eu(lds_waves_per_eu<Tr, S, EPI, NF, BM>())))
 void gemm_lds_kernel(GemmArgs a, LdsArgs L) {
   __shared__ __attribute__((aligned(16))) uint8_t lds[2][BM * LDS_ROW];
   const int tiles = count_tiles_lds(a, BM, L.min_rows, L.max_rows);
@@ -379,7 +384,8 @@ void gemm_lds_kernel(GemmArgs a, LdsArgs L) {
     row0 = __builtin_amdgcn_readfirstlane(row0);
     nrows = __builtin_amdgcn_readfirstlane(nrows);
     out0 = __builtin_amdgcn_readfirstlane(out0);
-    gemm_lds_tile<Tr, S, EPI, NF, BM>(a, L, lds, g, row0, nrows, out0, nblock, blockIdx.z);
+    gemm_lds_tile<Tr, S, EPI, NF, BM, ring_steps<Tr, S, EPI, NF, BM>()>(a, L, lds, g, row0, nrows, out0, nblock,
+                                                                          blockIdx.z);
   }
 }
 
@@ -452,52 +458,52 @@ __global__ __launch_bounds__(256) void gemm_reduce_kernel(GemmArgs a, LdsArgs L)
 int lds_chunk_elems(GemmElem elem) { return CH_BYTES / (elem == ELEM_F32 ? 4 : (elem == ELEM_BF16 ? 2 : 1)); }
 
 template <class Tr, int S, int EPI, int NF, int BM>
-static hipError_t launch_lds_one(const GemmArgs& a, const LdsArgs& L, hipStream_t stream) {
+static hipError_t launch_lds_one(const GemmArgs& a, const LdsArgs& L, hipStream_t stream, KernelEvents ev) {
   // persistent grid: at most `tiles_y` m-tiles per column block exist
   const long bound = long(ceil_div(a.N, WG_WAVES * NF)) * a.tiles_y;
   const int nwg = int(std::max(8L, std::min(bound, long(L.max_wgs)) / 8 * 8));
   const dim3 grid(nwg, 1, L.splits);
-  hipLaunchKernelGGL((gemm_lds_kernel<Tr, S, EPI, NF, BM>), grid, dim3(WG_THREADS), 0, stream, a, L);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess || L.splits == 1) return e;
+  const bool reduce = L.splits > 1 && !L.fold_reduce;
+  hipError_t e = launch_timed((gemm_lds_kernel<Tr, S, EPI, NF, BM>), grid, dim3(WG_THREADS), stream, ev.start,
+                              reduce ? nullptr : ev.stop, a, L);
+  if (e != hipSuccess || !reduce) return e;
   const size_t threads = size_t(L.part_rows) * (a.N / 4);
-  hipLaunchKernelGGL((gemm_reduce_kernel<typename Tr::part_t, EPI>), dim3(unsigned((threads + 255) / 256)), dim3(256),
-                     0, stream, a, L);
-  return hipGetLastError();
+  return launch_timed((gemm_reduce_kernel<typename Tr::part_t, EPI>), dim3(unsigned((threads + 255) / 256)),
+                      dim3(256), stream, nullptr, ev.stop, a, L);
 }
 
 // Products with two or three weight planes always use 32 features per
 // wavefront: the 64-feature, 128-row tile would need more than the 512
 // registers of a lane.
 template <class Tr, int S, int EPI>
-static hipError_t launch_lds_shape(const GemmArgs& a, const LdsArgs& L, hipStream_t stream) {
+static hipError_t launch_lds_shape(const GemmArgs& a, const LdsArgs& L, hipStream_t stream, KernelEvents ev) {
   if (S >= 2 || L.wave_features == 32) {
-    return L.tile_rows == 64 ? launch_lds_one<Tr, S, EPI, 32, 64>(a, L, stream)
-                             : launch_lds_one<Tr, S, EPI, 32, 128>(a, L, stream);
+    return L.tile_rows == 64 ? launch_lds_one<Tr, S, EPI, 32, 64>(a, L, stream, ev)
+                             : launch_lds_one<Tr, S, EPI, 32, 128>(a, L, stream, ev);
   }
   if constexpr (S == 1) {
-    return L.tile_rows == 64 ? launch_lds_one<Tr, S, EPI, 64, 64>(a, L, stream)
-                             : launch_lds_one<Tr, S, EPI, 64, 128>(a, L, stream);
+    return L.tile_rows == 64 ? launch_lds_one<Tr, S, EPI, 64, 64>(a, L, stream, ev)
+                             : launch_lds_one<Tr, S, EPI, 64, 128>(a, L, stream, ev);
   }
   return hipErrorInvalidValue;
 }
 
 hipError_t launch_gemm_lds(const GemmArgs& a, const LdsArgs& L, GemmElem elem, int planes, GemmEpi epi,
-                           hipStream_t stream) {
-  if (a.tiles_y <= 0) return hipSuccess;
+                           hipStream_t stream, KernelEvents ev) {
+  if (a.tiles_y <= 0) return record_events(ev.start, ev.stop, stream);
   if (epi == EPI_SWIGLU) {
     switch (elem) {
-      case ELEM_BF16: return launch_lds_shape<M32BF16, 2, EPI_SWIGLU>(a, L, stream);
-      case ELEM_I8: return launch_lds_shape<M32I8, 2, EPI_SWIGLU>(a, L, stream);
-      case ELEM_F32: return launch_lds_shape<M32F32, 2, EPI_SWIGLU>(a, L, stream);
+      case ELEM_BF16: return launch_lds_shape<M32BF16, 2, EPI_SWIGLU>(a, L, stream, ev);
+      case ELEM_I8: return launch_lds_shape<M32I8, 2, EPI_SWIGLU>(a, L, stream, ev);
+      case ELEM_F32: return launch_lds_shape<M32F32, 2, EPI_SWIGLU>(a, L, stream, ev);
     }
   } else {
     switch (elem) {
       case ELEM_BF16:
-        return planes == 3 ? launch_lds_shape<M32BF16, 3, EPI_SUM>(a, L, stream)
-                           : launch_lds_shape<M32BF16, 1, EPI_SUM>(a, L, stream);
-      case ELEM_I8: return launch_lds_shape<M32I8, 1, EPI_SUM>(a, L, stream);
-      case ELEM_F32: return launch_lds_shape<M32F32, 1, EPI_SUM>(a, L, stream);
+        return planes == 3 ? launch_lds_shape<M32BF16, 3, EPI_SUM>(a, L, stream, ev)
+                           : launch_lds_shape<M32BF16, 1, EPI_SUM>(a, L, stream, ev);
+      case ELEM_I8: return launch_lds_shape<M32I8, 1, EPI_SUM>(a, L, stream, ev);
+      case ELEM_F32: return launch_lds_shape<M32F32, 1, EPI_SUM>(a, L, stream, ev);
     }
   }
   return hipErrorInvalidValue;

@@ -51,8 +51,16 @@ struct GemmArgs {
   int ksplit;                // streaming kernel: wavefronts sharing a column tile (1, 2 or 4)
 };
 
+// Timing events a launcher attaches to its first / last kernel: the runtime
+// stamps them when that kernel starts / ends (hipExtLaunchKernel), so their
+// elapsed time is the kernels' own duration, with no marker between kernels.
+struct KernelEvents {
+  hipEvent_t start = nullptr;
+  hipEvent_t stop = nullptr;
+};
+
 hipError_t launch_gemm(const GemmArgs& a, GemmElem elem, int planes, GemmEpi epi,
-                       hipStream_t stream);
+                       hipStream_t stream, KernelEvents ev = {});
 
 // Upper bound on the m-tiles of grouped rows (R rows over G groups), and the
 // m-tiles of one dense group of `rows` rows.
@@ -78,23 +86,40 @@ struct LdsArgs {
   void* partial;       // splits > 1: [splits][part_rows][acc planes * N] fp32 / int32
   int part_rows;
   int max_wgs;         // cap of the persistent grid (workgroups per split)
+  int fold_reduce;     // splits > 1: launch no reduce pass; the consumer adds
+                       // the partial sums in split order (router -> gate)
 };
 hipError_t launch_gemm_lds(const GemmArgs& a, const LdsArgs& L, GemmElem elem, int planes, GemmEpi epi,
-                           hipStream_t stream);
+                           hipStream_t stream, KernelEvents ev = {});
 int lds_chunk_elems(GemmElem elem);
 
 // ---------------------------------------------------------------------------
 // Gating + top-k (route.hip)
 // ---------------------------------------------------------------------------
 struct GateArgs {
-  const float* z;   // [T][ldz] logits, bias included
+  const float* z;   // [T][ldz] logits, bias included (partial == nullptr)
   int ldz;
   int T, E, k, gate, n_group, topk_group, per_group_k, renorm;
   float route_scale;
   int* topk_idx;
   float* topk_w;
+  const float* partial;   // or: [splits][T][ldz] split-K partial sums of x W_r,
+  int splits;             //   added in split order, then
+  const float* bias;      //   the logit bias [E] (may be null)
 };
 hipError_t launch_gate(const GateArgs& a, hipStream_t stream);
+
+// Router product for few tokens (route.hip): z[T][e_pad] = x W_r + bias with
+// 16 tokens x 16 experts per workgroup and the reduction split over its
+// wavefronts; no split-K partials, no reduce pass.
+struct RouterArgs {
+  const uint8_t* w;   // packed router fragments (1 fp32 plane or 3 bf16 planes)
+  const uint8_t* x;   // [T][K] fp32 (1 plane) or bf16 (3 planes)
+  int T, K, E, e_pad;
+  const float* bias;  // [E] or null
+  float* z;           // [T][e_pad]
+};
+hipError_t launch_router_small(const RouterArgs& a, bool f32, hipStream_t stream);
 
 // ---------------------------------------------------------------------------
 // Stable counting sort of slots by expert (permute.hip)

@@ -1,38 +1,85 @@
-// Gating and top-k selection for gfx950: one wavefront per token.
+// Gating and top-k selection for gfx950: one token per row of 16 lanes,
+// four tokens per wavefront.
 //
-// The router matmul (gemm.hip) leaves the logits z = x W_r + b in a
-// [T][E_pad] buffer. Here each wavefront takes one token: lane l holds
-// experts l, l+64, l+128, l+192. Scores are the softmax over the E logits or
-// the logistic sigmoid of each (the pages give no gate formula; which one a
-// workload uses is part of its descriptor). Selection runs as rounds of a
-// wavefront-wide argmax over a 64-bit key (order-preserving bits of the
-// logit, then the complemented expert id, so the larger logit wins and equal
-// logits go to the lower id) exchanged with cross-lane shuffles:
+// The router product leaves the logits z = x W_r + b in a [T][E_pad] buffer
+// (or split-K partial sums that are added here in split order, then the
+// bias). Lane r of a row holds experts r, r+16, r+32, ... (PL of them).
+// Scores are the softmax over the E logits or the logistic sigmoid of each
+// (the pages give no gate formula; which one a workload uses is part of its
+// descriptor). Every reduction stays inside the row, as data-parallel moves
+// after which all 16 lanes hold the result, so rounds cost a few
+// instructions and never leave the vector unit. A selection round is an
+// argmax: the largest order-preserving bits of the logit, then the lowest
+// expert id holding them (equal logits go to the lower id):
 //  - plain top-k: k rounds over all experts;
 //  - group-limited: group scores (sum of the two largest scores of each
-//    contiguous group, reduced with shuffles), topk_group rounds over the
-//    groups, then k rounds over the experts of the kept groups;
+//    contiguous group), topk_group rounds over the groups, then k rounds over
+//    the experts of the kept groups;
 //  - per-group quota (the grouped experts of Pangu Pro MoE, page
 //    "华为技术披露集 VOL.12：昇腾×盘古", opening section): per_group_k rounds
 //    inside each group, then k rounds to order the chosen by score.
 // Softmax and sigmoid are monotone, so selecting on the logit is selecting
 // on the score. Weights are the selected scores, renormalised over the k
 // selections when asked, times route_scale.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
 namespace moe {
 
-constexpr int GATE_PER_LANE = 4;   // E <= 256
+constexpr int ROW = 16;            // lanes per token
+constexpr int GATE_TOKENS = WAVE / ROW;
+constexpr int GROUP_SLOTS = 4;     // group-limited routing: n_group <= 64
 
 __device__ inline uint32_t order_bits(float f) {
   const uint32_t b = __float_as_uint(f + 0.0f);   // -0 -> +0
   return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
 }
-__device__ inline uint64_t make_key(float v, int id) {
-  return (uint64_t(order_bits(v)) << 32) | uint64_t(0xFFFFFFFFu - uint32_t(id));
+
+// Reductions over the 16 lanes of a row; every lane of the row gets the result.
+__device__ inline uint32_t row_max_u32(uint32_t v) {
+  v = max(v, dpp_u32<DPP_QUAD_1032>(v));
+  v = max(v, dpp_u32<DPP_QUAD_2301>(v));
+  v = max(v, dpp_u32<DPP_ROW_HALF_MIRROR>(v));
+  return max(v, dpp_u32<DPP_ROW_MIRROR>(v));
 }
-__device__ inline int key_id(uint64_t key) { return int(0xFFFFFFFFu - uint32_t(key)); }
+__device__ inline uint32_t row_min_u32(uint32_t v) {
+  v = min(v, dpp_u32<DPP_QUAD_1032>(v));
+  v = min(v, dpp_u32<DPP_QUAD_2301>(v));
+  v = min(v, dpp_u32<DPP_ROW_HALF_MIRROR>(v));
+  return min(v, dpp_u32<DPP_ROW_MIRROR>(v));
+}
+__device__ inline float row_max_f32(float v) {
+  return row_reduce_f32(v, [](float x, float y) { return fmaxf(x, y); });
+}
+__device__ inline float row_sum_f32(float v) {
+  return row_reduce_f32(v, [](float x, float y) { return x + y; });
+}
+
+// Lowest id (slot i of lane r is id i*16 + r) among the candidates holding
+// the largest order bits; -1 when there is no candidate (every finite logit
+// has order bits above 0).
+template <int N>
+__device__ inline int row_argmax(const uint32_t (&ob)[N], const bool (&cand)[N], int r) {
+  uint32_t m = 0;
+#pragma unroll
+  for (int i = 0; i < N; ++i) m = max(m, cand[i] ? ob[i] : 0u);
+  m = row_max_u32(m);
+  uint32_t best = 0xFFFFFFFFu;
+#pragma unroll
+  for (int i = N - 1; i >= 0; --i)
+    if (cand[i] && ob[i] == m) best = uint32_t(i * ROW + r);
+  best = row_min_u32(best);
+  return m == 0 ? -1 : int(best);
+}
+
+template <int N>
+__device__ inline void drop(bool (&cand)[N], int id, int r) {
+#pragma unroll
+  for (int i = 0; i < N; ++i)
+    if (i * ROW + r == id) cand[i] = false;
+}
 
 // Top two of (a1 >= a2) and (b1 >= b2).
 __device__ inline void merge_top2(float& a1, float& a2, float b1, float b2) {
@@ -43,138 +90,260 @@ __device__ inline void merge_top2(float& a1, float& a2, float b1, float b2) {
     a2 = fmaxf(a2, b1);
   }
 }
+template <int CTRL>
+__device__ inline void merge_top2_dpp(float& t1, float& t2) {
+  const float b1 = dpp_f32<CTRL>(t1), b2 = dpp_f32<CTRL>(t2);
+  merge_top2(t1, t2, b1, b2);
+}
 
-__global__ __launch_bounds__(256) void gate_topk_kernel(GateArgs a) {
-  const int lane = threadIdx.x & (WAVE - 1);
-  const int t = blockIdx.x * (blockDim.x / WAVE) + threadIdx.x / WAVE;
-  if (t >= a.T) return;
-  const float* zt = a.z + size_t(t) * a.ldz;
+template <int PL>
+__global__ __launch_bounds__(WAVE) void gate_topk_kernel(GateArgs a) {
+  __shared__ float sc_lds[GATE_TOKENS][PL * ROW];
+  const int lane = threadIdx.x;
+  const int r = lane & (ROW - 1), row = lane / ROW;
+  const int t_raw = blockIdx.x * GATE_TOKENS + row;
+  const bool live = t_raw < a.T;            // dead rows work on a valid token and write nothing
+  const int t = live ? t_raw : a.T - 1;
 
-  float u[GATE_PER_LANE], sc[GATE_PER_LANE];
-  bool valid[GATE_PER_LANE];
+  float u[PL], sc[PL];
+  uint32_t ob[PL];
+  bool valid[PL];
+  int grp[PL];
 #pragma unroll
-  for (int i = 0; i < GATE_PER_LANE; ++i) {
-    const int e = lane + i * WAVE;
+  for (int i = 0; i < PL; ++i) {
+    const int e = i * ROW + r;
     valid[i] = e < a.E;
-    u[i] = valid[i] ? zt[e] : -INFINITY;
+    u[i] = 0.f;
   }
+  if (!a.partial) {
+#pragma unroll
+    for (int i = 0; i < PL; ++i)
+      if (valid[i]) u[i] = a.z[size_t(t) * a.ldz + i * ROW + r];
+  } else {
+    for (int sp = 0; sp < a.splits; ++sp) {
+      const float* P = a.partial + (size_t(sp) * a.T + t) * a.ldz + r;
+#pragma unroll
+      for (int i = 0; i < PL; ++i)
+        if (valid[i]) u[i] += P[i * ROW];
+    }
+    if (a.bias) {
+#pragma unroll
+      for (int i = 0; i < PL; ++i)
+        if (valid[i]) u[i] += a.bias[i * ROW + r];
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < PL; ++i) {
+    if (!valid[i]) u[i] = -INFINITY;
+    ob[i] = order_bits(u[i]);
+  }
+
   if (a.gate == MOE_GATE_SOFTMAX) {
     float m = -INFINITY;
 #pragma unroll
-    for (int i = 0; i < GATE_PER_LANE; ++i) m = fmaxf(m, u[i]);
-    m = wave_max(m);
-    float ex[GATE_PER_LANE], sum = 0.f;
+    for (int i = 0; i < PL; ++i) m = fmaxf(m, u[i]);
+    m = row_max_f32(m);
+    float sum = 0.f;
 #pragma unroll
-    for (int i = 0; i < GATE_PER_LANE; ++i) {
-      ex[i] = valid[i] ? expf(u[i] - m) : 0.f;
-      sum += ex[i];
+    for (int i = 0; i < PL; ++i) {
+      sc[i] = valid[i] ? expf(u[i] - m) : 0.f;
+      sum += sc[i];
     }
-    sum = wave_sum(sum);
+    sum = row_sum_f32(sum);
 #pragma unroll
-    for (int i = 0; i < GATE_PER_LANE; ++i) sc[i] = ex[i] / sum;
+    for (int i = 0; i < PL; ++i) sc[i] = sc[i] / sum;
   } else {
 #pragma unroll
-    for (int i = 0; i < GATE_PER_LANE; ++i) sc[i] = valid[i] ? 1.0f / (1.0f + expf(-u[i])) : 0.f;
+    for (int i = 0; i < PL; ++i) sc[i] = valid[i] ? 1.0f / (1.0f + expf(-u[i])) : 0.f;
   }
-
-  // Candidate mask per owned expert.
-  bool cand[GATE_PER_LANE];
 #pragma unroll
-  for (int i = 0; i < GATE_PER_LANE; ++i) cand[i] = valid[i];
-  const int gsize = a.E / a.n_group;
+  for (int i = 0; i < PL; ++i) sc_lds[row][i * ROW + r] = sc[i];
 
+  bool cand[PL];
+#pragma unroll
+  for (int i = 0; i < PL; ++i) cand[i] = valid[i];
+
+  if (a.topk_group > 0 || a.per_group_k > 0) {
+    const int gsize = a.E / a.n_group;
+#pragma unroll
+    for (int i = 0; i < PL; ++i) grp[i] = valid[i] ? (i * ROW + r) / gsize : -1;
+  }
   if (a.topk_group > 0) {
-    // group score = sum of the two largest scores; lane g keeps group g's score.
-    float my_gs = -INFINITY;
+    // group g's score = sum of its two largest scores; slot g/16 of lane g%16
+    float gs[GROUP_SLOTS];
+    bool gc[GROUP_SLOTS];
+#pragma unroll
+    for (int j = 0; j < GROUP_SLOTS; ++j) {
+      gs[j] = -INFINITY;
+      gc[j] = j * ROW + r < a.n_group;
+    }
     for (int g = 0; g < a.n_group; ++g) {
       float t1 = -INFINITY, t2 = -INFINITY;
 #pragma unroll
-      for (int i = 0; i < GATE_PER_LANE; ++i) {
-        const int e = lane + i * WAVE;
-        if (valid[i] && e / gsize == g) merge_top2(t1, t2, sc[i], -INFINITY);
-      }
+      for (int i = 0; i < PL; ++i)
+        if (grp[i] == g) merge_top2(t1, t2, sc[i], -INFINITY);
+      merge_top2_dpp<DPP_QUAD_1032>(t1, t2);
+      merge_top2_dpp<DPP_QUAD_2301>(t1, t2);
+      merge_top2_dpp<DPP_ROW_HALF_MIRROR>(t1, t2);
+      merge_top2_dpp<DPP_ROW_MIRROR>(t1, t2);
 #pragma unroll
-      for (int o = 32; o > 0; o >>= 1) {
-        const float b1 = __shfl_xor(t1, o, WAVE);
-        const float b2 = __shfl_xor(t2, o, WAVE);
-        merge_top2(t1, t2, b1, b2);
-      }
-      if (lane == g) my_gs = t1 + t2;
+      for (int j = 0; j < GROUP_SLOTS; ++j)
+        if (j * ROW + r == g) gs[j] = t1 + t2;
     }
+    uint32_t gob[GROUP_SLOTS];
+#pragma unroll
+    for (int j = 0; j < GROUP_SLOTS; ++j) gob[j] = order_bits(gs[j]);
     uint64_t kept = 0;
-    for (int r = 0; r < a.topk_group; ++r) {
-      const bool live = lane < a.n_group && !((kept >> lane) & 1ull);
-      const uint64_t best = wave_max_u64(live ? make_key(my_gs, lane) : 0ull);
-      kept |= 1ull << key_id(best);
+    for (int q = 0; q < a.topk_group; ++q) {
+      const int gw = row_argmax(gob, gc, r);
+      if (gw < 0) break;
+      kept |= 1ull << gw;
+      drop(gc, gw, r);
     }
 #pragma unroll
-    for (int i = 0; i < GATE_PER_LANE; ++i) {
-      const int e = lane + i * WAVE;
-      cand[i] = valid[i] && ((kept >> (e / gsize)) & 1ull);
-    }
+    for (int i = 0; i < PL; ++i) cand[i] = valid[i] && ((kept >> grp[i]) & 1ull);
   } else if (a.per_group_k > 0) {
-    bool chosen[GATE_PER_LANE] = {false, false, false, false};
+    bool chosen[PL];
+#pragma unroll
+    for (int i = 0; i < PL; ++i) chosen[i] = false;
     for (int g = 0; g < a.n_group; ++g) {
-      for (int r = 0; r < a.per_group_k; ++r) {
-        uint64_t mine = 0;
+      bool in_g[PL];
 #pragma unroll
-        for (int i = 0; i < GATE_PER_LANE; ++i) {
-          const int e = lane + i * WAVE;
-          if (valid[i] && !chosen[i] && e / gsize == g) {
-            const uint64_t kk = make_key(u[i], e);
-            mine = kk > mine ? kk : mine;
-          }
-        }
-        const int win = key_id(wave_max_u64(mine));
+      for (int i = 0; i < PL; ++i) in_g[i] = grp[i] == g;
+      for (int q = 0; q < a.per_group_k; ++q) {
+        const int win = row_argmax(ob, in_g, r);
+        if (win < 0) break;
+        drop(in_g, win, r);
 #pragma unroll
-        for (int i = 0; i < GATE_PER_LANE; ++i)
-          if (lane + i * WAVE == win) chosen[i] = true;
+        for (int i = 0; i < PL; ++i)
+          if (i * ROW + r == win) chosen[i] = true;
       }
     }
 #pragma unroll
-    for (int i = 0; i < GATE_PER_LANE; ++i) cand[i] = chosen[i];
+    for (int i = 0; i < PL; ++i) cand[i] = chosen[i];
   }
 
-  // k rounds over the candidates, descending logit, ties to the lower id.
-  int sel_e = 0;
-  float sel_s = 0.f, total = 0.f;
+  // k rounds over the candidates: descending logit, ties to the lower id;
+  // lane r of the row keeps selection r.
+  int sel_e = -1;
   for (int j = 0; j < a.k; ++j) {
-    uint64_t mine = 0;
-#pragma unroll
-    for (int i = 0; i < GATE_PER_LANE; ++i) {
-      if (cand[i]) {
-        const uint64_t kk = make_key(u[i], lane + i * WAVE);
-        mine = kk > mine ? kk : mine;
-      }
-    }
-    const int win = key_id(wave_max_u64(mine));
-    float s_own = 0.f;
-#pragma unroll
-    for (int i = 0; i < GATE_PER_LANE; ++i) {
-      if (lane + i * WAVE == win) {
-        cand[i] = false;
-        s_own = sc[i];
-      }
-    }
-    const float s_win = __shfl(s_own, win & (WAVE - 1), WAVE);
-    total += s_win;
-    if (lane == j) {
-      sel_e = win;
-      sel_s = s_win;
-    }
+    const int win = row_argmax(ob, cand, r);
+    if (win < 0) break;
+    drop(cand, win, r);
+    if (r == j) sel_e = win;
   }
-  if (lane < a.k) {
-    float wv = a.renorm ? sel_s / total : sel_s;
+  __syncthreads();   // scores of the row are in LDS
+  const bool mine = r < a.k && sel_e >= 0;
+  const float s = mine ? sc_lds[row][sel_e] : 0.f;
+  const float total = row_sum_f32(s);
+  if (live && r < a.k) {
+    float wv = a.renorm ? s / total : s;
     wv *= a.route_scale;
-    a.topk_idx[size_t(t) * a.k + lane] = sel_e;
-    a.topk_w[size_t(t) * a.k + lane] = wv;
+    a.topk_idx[size_t(t) * a.k + r] = sel_e;
+    a.topk_w[size_t(t) * a.k + r] = wv;
   }
 }
 
 hipError_t launch_gate(const GateArgs& a, hipStream_t stream) {
   if (a.T <= 0) return hipSuccess;
-  constexpr int waves = 4;
-  hipLaunchKernelGGL(gate_topk_kernel, dim3(ceil_div(a.T, waves)), dim3(waves * WAVE), 0, stream, a);
+  const dim3 grid(ceil_div(a.T, GATE_TOKENS)), block(WAVE);
+  const int pl = ceil_div(a.E, ROW);
+  if (pl <= 1) hipLaunchKernelGGL(gate_topk_kernel<1>, grid, block, 0, stream, a);
+  else if (pl <= 2) hipLaunchKernelGGL(gate_topk_kernel<2>, grid, block, 0, stream, a);
+  else if (pl <= 4) hipLaunchKernelGGL(gate_topk_kernel<4>, grid, block, 0, stream, a);
+  else if (pl <= 6) hipLaunchKernelGGL(gate_topk_kernel<6>, grid, block, 0, stream, a);
+  else if (pl <= 8) hipLaunchKernelGGL(gate_topk_kernel<8>, grid, block, 0, stream, a);
+  else if (pl <= 12) hipLaunchKernelGGL(gate_topk_kernel<12>, grid, block, 0, stream, a);
+  else hipLaunchKernelGGL(gate_topk_kernel<16>, grid, block, 0, stream, a);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Router product for few tokens: one workgroup per 16 tokens x 16 experts.
+// Its RW wavefronts split the reduction (ROUTER_U fragments per batch, the
+// next batch's loads issued before the current batch's matrix-core ops) and
+// add their partial tiles in wavefront order through LDS, so the result is
+// fixed by the shape alone. Operand A is the packed router fragment (16
+// experts), operand B the 16 token rows; with three bf16 planes the three
+// products accumulate into one fp32 tile, which equals x times the fp32
+// router up to fp32 accumulation.
+// ---------------------------------------------------------------------------
+constexpr int ROUTER_WAVES = 8;
+constexpr int ROUTER_U = 4;
+
+template <class Tr, int S>
+__global__ __launch_bounds__(ROUTER_WAVES * WAVE) void router_small_kernel(RouterArgs a) {
+  constexpr int FB = frag_bytes<Tr>();
+  constexpr int XB = Tr::KF * int(sizeof(typename Tr::elem_t));   // x bytes per fragment step
+  using op_t = typename Tr::op_t;
+  __shared__ f32x4 red[ROUTER_WAVES][WAVE];
+
+  const int lane = threadIdx.x & (WAVE - 1);
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x / WAVE);   // wavefront-uniform
+  const int t0 = blockIdx.x * ROW_BLOCK, nt = blockIdx.y;
+  const int KT = a.K / Tr::KF;
+  const int kt0 = wv * KT / ROUTER_WAVES, kt1 = (wv + 1) * KT / ROUTER_WAVES;
+  const uint8_t* wp = a.w + size_t(nt) * KT * S * FB + size_t(lane) * Tr::BPL;
+  const int tok = min(t0 + (lane & 15), a.T - 1);
+  const uint8_t* xp = a.x + size_t(tok) * a.K * sizeof(typename Tr::elem_t) + (lane >> 4) * Tr::BPL;
+
+  typename Tr::acc_t acc = Tr::zero();
+  op_t xa[2][ROUTER_U], wb[2][ROUTER_U][S];
+  // Buffers are chosen by compile-time constants only (no dynamic indexing
+  // of register arrays).
+  auto load = [&](auto buf, int kt) {
+#pragma unroll
+    for (int u = 0; u < ROUTER_U; ++u) {
+      const int k = min(kt + u, kt1 - 1);   // clamped: every address is inside the operands
+      xa[buf][u] = Tr::load(xp + size_t(k) * XB);
+#pragma unroll
+      for (int p = 0; p < S; ++p) wb[buf][u][p] = Tr::load(wp + (size_t(k) * S + p) * FB);
+    }
+  };
+  auto compute = [&](auto buf, int kt) {
+#pragma unroll
+    for (int u = 0; u < ROUTER_U; ++u) {
+      if (kt + u < kt1) {
+#pragma unroll
+        for (int p = 0; p < S; ++p) acc = Tr::mfma(wb[buf][u][p], xa[buf][u], acc);
+      }
+    }
+  };
+  using B0 = std::integral_constant<int, 0>;
+  using B1 = std::integral_constant<int, 1>;
+  if (kt0 < kt1) {
+    load(B0{}, kt0);
+    for (int kt = kt0; kt < kt1; kt += 2 * ROUTER_U) {
+      if (kt + ROUTER_U < kt1) load(B1{}, kt + ROUTER_U);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(B0{}, kt);
+      if (kt + 2 * ROUTER_U < kt1) load(B0{}, kt + 2 * ROUTER_U);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(B1{}, kt + ROUTER_U);
+    }
+  }
+  red[wv][lane] = f32x4{Tr::to_f32(acc, 0), Tr::to_f32(acc, 1), Tr::to_f32(acc, 2), Tr::to_f32(acc, 3)};
+  __syncthreads();
+  // thread (j, l) of the first four wavefronts: expert (l/16)*4 + j, token l%16
+  if (threadIdx.x < 4 * WAVE) {
+    const int l = threadIdx.x & (WAVE - 1), j = threadIdx.x / WAVE;
+    float v = 0.f;
+#pragma unroll
+    for (int w = 0; w < ROUTER_WAVES; ++w) v += red[w][l][j];
+    const int e = nt * TILE_N + (l >> 4) * 4 + j;
+    const int t = t0 + (l & 15);
+    if (a.bias && e < a.E) v += a.bias[e];
+    if (t < a.T) a.z[size_t(t) * a.e_pad + e] = v;
+  }
+}
+
+hipError_t launch_router_small(const RouterArgs& a, bool f32, hipStream_t stream) {
+  if (a.T <= 0) return hipSuccess;
+  const dim3 grid(ceil_div(a.T, ROW_BLOCK), a.e_pad / TILE_N), block(ROUTER_WAVES * WAVE);
+  if (f32)
+    hipLaunchKernelGGL((router_small_kernel<TrF32, 1>), grid, block, 0, stream, a);
+  else
+    hipLaunchKernelGGL((router_small_kernel<TrBF16, 3>), grid, block, 0, stream, a);
   return hipGetLastError();
 }
 

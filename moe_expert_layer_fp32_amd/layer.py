@@ -10,6 +10,7 @@ import numpy as np
 import torch
 
 from . import lib as L
+from .hip_events import Event
 
 
 def to_device(a: np.ndarray, device="cuda") -> torch.Tensor:
@@ -26,26 +27,19 @@ def empty_bytes(n: int, device="cuda") -> torch.Tensor:
     return torch.empty(max(int(n), 1), dtype=torch.uint8, device=device)
 
 
-def event_handle(ev: torch.cuda.Event) -> int:
-    """The hipEvent_t behind a torch event (torch creates it on first record)."""
-    if ev.cuda_event == 0:
-        ev.record()
-    return ev.cuda_event
-
-
 class SecondStream:
     """A second stream of default priority with the fork/join events that
     moe_aux takes for running the shared expert concurrently."""
 
     def __init__(self, device="cuda"):
         self.stream = torch.cuda.Stream(device=device)
-        self.fork = torch.cuda.Event()
-        self.join = torch.cuda.Event()
+        self.fork = Event(timing=False)
+        self.join = Event(timing=False)
 
     def fill(self, aux: L.MoeAux) -> L.MoeAux:
         aux.stream2 = self.stream.cuda_stream
-        aux.ev_fork = event_handle(self.fork)
-        aux.ev_join = event_handle(self.join)
+        aux.ev_fork = self.fork.handle
+        aux.ev_join = self.join.handle
         return aux
 
 
