@@ -117,6 +117,24 @@ struct TrF32 {
 template <class Tr>
 __host__ __device__ constexpr int frag_bytes() { return FRAG_LANES * Tr::BPL; }
 
+// Packed weight layout of one matrix (one expert): fragments of 16 columns
+// (ntile nt) x KF reduction elements (step kt) of each plane s, grouped in
+// column blocks of FRAG_BLOCK fragments; inside a block the order is
+// [kt][s][fragment], so the 128 columns a workgroup of the tiled kernel owns
+// are one contiguous stretch of memory, read front to back (per-workgroup
+// contiguous streams keep the HBM rows open; one stream per fragment column
+// does not). The last block of a matrix may be narrower.
+constexpr int FRAG_BLOCK = 8;
+__host__ __device__ inline int frag_block_width(int nt, int NT) {
+  const int b0 = nt / FRAG_BLOCK * FRAG_BLOCK;
+  return NT - b0 < FRAG_BLOCK ? NT - b0 : FRAG_BLOCK;
+}
+__host__ __device__ inline size_t frag_offset(int nt, int kt, int s, int NT, int KT, int S, int FB) {
+  const int cb = nt / FRAG_BLOCK, j = nt % FRAG_BLOCK;
+  const int w = frag_block_width(nt, NT);
+  return (size_t(cb) * FRAG_BLOCK * KT * S + (size_t(kt) * S + s) * w + j) * size_t(FB);
+}
+
 // ---------------------------------------------------------------------------
 // wavefront reductions
 //

@@ -11,8 +11,8 @@
 // column tiles of 16 times WK slices of the reduction (WK = 1, 2 or 4, chosen
 // on the host so that the device has enough wavefronts streaming; the WK
 // partial sums are added through LDS in a fixed order). Every wavefront
-// streams its own weight fragments straight from HBM into registers - the
-// packed layout makes each fragment load one contiguous 1 KiB read - and
+// streams its own weight fragments straight from HBM into registers - each
+// fragment load is one contiguous 1 KiB read - and
 // never shares them, so each weight byte of a tile is read exactly once; the
 // loads run a fixed number of steps ahead of the matrix cores, which is what
 // keeps enough bytes in flight for HBM. An expert with few tokens therefore
@@ -133,7 +133,9 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int g, int row0, in
       const int brow = a.sorted_slot ? a.sorted_slot[row0 + r] / a.k : out0 + r;
       bp[mb] = a.B + size_t(brow) * a.ldb + (lane >> 4) * Tr::BPL + size_t(kt0) * BSTEP;
     }
-    const uint8_t* ap = a.A + size_t(g) * a.a_group_stride + (size_t(ntile) * KT + kt0) * S * FB + lane * Tr::BPL;
+    const int NT = a.N / TILE_N;
+    const size_t FBW = size_t(frag_block_width(ntile, NT)) * FB;   // stride of one plane step
+    const uint8_t* ap = a.A + size_t(g) * a.a_group_stride + frag_offset(ntile, kt0, 0, NT, KT, S, FB) + lane * Tr::BPL;
 
     op_t wq[D][S];
     op_t bq[D][MB];
@@ -142,7 +144,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int g, int row0, in
     // every path and the waits before each stage only drain that stage.
     auto load_stage = [&](int p, int kt) {
 #pragma unroll
-      for (int s = 0; s < S; ++s) wq[p][s] = Tr::load(ap + size_t(kt * S + s) * FB);
+      for (int s = 0; s < S; ++s) wq[p][s] = Tr::load(ap + size_t(kt * S + s) * FBW);
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) bq[p][mb] = Tr::load(bp[mb] + size_t(kt) * BSTEP);
     };

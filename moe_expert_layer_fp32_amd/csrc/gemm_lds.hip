@@ -180,8 +180,12 @@ __device__ __forceinline__ void gemm_lds_tile(const GemmArgs& a, const LdsArgs& 
   const bool wave_live = ft_first * 32 < a.N;
   const int ft0 = wave_live ? ft_first : a.N / 32 - FT;
   const int r32 = lane & 31, half = lane >> 5;
-  const uint8_t* abase = a.A + size_t(g) * a.a_group_stride +
-                         size_t((2 * ft0 + (r32 >> 4)) * KT) * S * FB + (half * 16 + (r32 & 15)) * Tr::BPL;
+  // The wavefront's 2*FT fragment columns lie in one block of the packed
+  // layout (2*ft0 is a multiple of 2*FT, and 2*FT divides the block).
+  const int NT = a.N / 16;
+  const size_t FBW = size_t(frag_block_width(2 * ft0, NT)) * FB;   // stride of one plane step
+  const uint8_t* abase = a.A + size_t(g) * a.a_group_stride + frag_offset(2 * ft0 + (r32 >> 4), 0, 0, NT, KT, S, FB) +
+                         (half * 16 + (r32 & 15)) * Tr::BPL;
   // Ring of RA matrix-core steps of weight operands, refilled RA steps ahead
   // across chunk boundaries. Every load is unconditional (steps past the end
   // re-read the last one), so the waits only drain the step being used.
@@ -195,8 +199,7 @@ __device__ __forceinline__ void gemm_lds_tile(const GemmArgs& a, const LdsArgs& 
     for (int f = 0; f < FT; ++f)
 #pragma unroll
       for (int s = 0; s < S; ++s)
-        aring[slot][f][s] =
-            Tr::load(abase + (size_t(2 * f) * KT * S + size_t(kt) * S + s) * FB + h * 2 * 16 * Tr::BPL);
+        aring[slot][f][s] = Tr::load(abase + (size_t(kt) * S + s) * FBW + size_t(2 * f) * FB + h * 2 * 16 * Tr::BPL);
   };
 
 
@@ -360,9 +363,9 @@ __device__ __forceinline__ void gemm_lds_tile(const GemmArgs& a, const LdsArgs& 
 // workgroups on that XCD. Tiles sharing a weight column block thus run close
 // together in time on one L2.
 template <class Tr, int S, int EPI, int NF, int BM>
-constexpr int ring_steps() { return 8; }
+constexpr int ring_steps() { return S == 1 ? 8 : 4; }
 template <class Tr, int S, int EPI, int NF, int BM>
-constexpr int lds_waves_per_eu() { return BM == 64 && NF == 32 && ring_steps<Tr, S, EPI, NF, BM>() == 8 ? 2 : 1; }
+constexpr int lds_waves_per_eu() { return BM == 64 && NF == 32 && ring_steps<Tr, S, EPI, NF, BM>() <= 8 ? 2 : 1; }
 
 template <class Tr, int S, int EPI, int NF, int BM>
 __global__ __launch_bounds__(WG_THREADS) __attribute__((amdgpu_waves_per_eu(lds_waves_per_eu<Tr, S, EPI, NF, BM>())))

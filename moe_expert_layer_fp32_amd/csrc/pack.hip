@@ -4,9 +4,11 @@
 // 16 output columns x KF reduction elements, stored lane by lane exactly as
 // a wavefront loads it (lane l: column l % 16, reduction elements
 // (l / 16) * KF/4 ...), so one fragment is one contiguous 1 KiB (bf16,
-// int8) or 256 B (fp32) read. Fragments of a 16-column tile follow each
-// other along the reduction, with the planes of one step adjacent (W1 next
-// to W3 for the SwiGLU pair, or the three bf16 planes of the router).
+// int8) or 256 B (fp32) read. Blocks of 8 fragment columns (128 output
+// columns) are stored one after the other; inside a block, step by step
+// along the reduction, the planes of a step (W1 and W3 of the SwiGLU pair,
+// or the three bf16 planes of the router) and in each plane the block's
+// fragments side by side (frag_offset in common.h).
 //
 // Router planes: an fp32 weight w splits exactly into three bf16 values,
 // hi = bf16(w), mid = bf16(w - hi), lo = w - hi - mid (each residual is exact
@@ -38,7 +40,9 @@ __global__ void pack_experts_kernel(const typename Tr::elem_t* __restrict__ src0
     typename Tr::elem_t v[PER];
 #pragma unroll
     for (int j = 0; j < PER; ++j) v[j] = src[(size_t(g) * K + k0 + j) * N + n];
-    auto* out = reinterpret_cast<typename Tr::elem_t*>(dst + i * Tr::BPL);
+    constexpr int FB = frag_bytes<Tr>();
+    const size_t o = size_t(g) * NT * KT * planes * FB + frag_offset(nt, kt, p, NT, KT, planes, FB) + lane * Tr::BPL;
+    auto* out = reinterpret_cast<typename Tr::elem_t*>(dst + o);
 #pragma unroll
     for (int j = 0; j < PER; ++j) out[j] = v[j];
   }
@@ -61,10 +65,12 @@ __global__ void pack_router_kernel(const float* __restrict__ wr, int K, int E, u
     const int nt = int(r);
     const int n = nt * TILE_N + (lane & 15);
     const int k0 = kt * KF + (lane >> 4) * PER;
+    constexpr int BPL = PLANES == 1 ? TrF32::BPL : TrBF16::BPL;
+    const size_t o = frag_offset(nt, kt, p, NT, KT, PLANES, FRAG_LANES * BPL) + lane * BPL;
     if (PLANES == 1) {
-      reinterpret_cast<float*>(dst)[i] = n < E ? wr[size_t(k0) * E + n] : 0.f;
+      *reinterpret_cast<float*>(dst + o) = n < E ? wr[size_t(k0) * E + n] : 0.f;
     } else {
-      uint16_t* out = reinterpret_cast<uint16_t*>(dst + i * 16);
+      uint16_t* out = reinterpret_cast<uint16_t*>(dst + o);
 #pragma unroll
       for (int j = 0; j < PER; ++j) {
         const float w = n < E ? wr[size_t(k0 + j) * E + n] : 0.f;

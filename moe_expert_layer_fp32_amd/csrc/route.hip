@@ -283,7 +283,9 @@ __global__ __launch_bounds__(ROUTER_WAVES * WAVE) void router_small_kernel(Route
   const int t0 = blockIdx.x * ROW_BLOCK, nt = blockIdx.y;
   const int KT = a.K / Tr::KF;
   const int kt0 = wv * KT / ROUTER_WAVES, kt1 = (wv + 1) * KT / ROUTER_WAVES;
-  const uint8_t* wp = a.w + size_t(nt) * KT * S * FB + size_t(lane) * Tr::BPL;
+  const int NT = a.e_pad / TILE_N;
+  const size_t FBW = size_t(frag_block_width(nt, NT)) * FB;   // stride of one plane step
+  const uint8_t* wp = a.w + frag_offset(nt, 0, 0, NT, KT, S, FB) + size_t(lane) * Tr::BPL;
   const int tok = min(t0 + (lane & 15), a.T - 1);
   const uint8_t* xp = a.x + size_t(tok) * a.K * sizeof(typename Tr::elem_t) + (lane >> 4) * Tr::BPL;
 
@@ -297,7 +299,7 @@ __global__ __launch_bounds__(ROUTER_WAVES * WAVE) void router_small_kernel(Route
       const int k = min(kt + u, kt1 - 1);   // clamped: every address is inside the operands
       xa[buf][u] = Tr::load(xp + size_t(k) * XB);
 #pragma unroll
-      for (int p = 0; p < S; ++p) wb[buf][u][p] = Tr::load(wp + (size_t(k) * S + p) * FB);
+      for (int p = 0; p < S; ++p) wb[buf][u][p] = Tr::load(wp + (size_t(k) * S + p) * FBW);
     }
   };
   auto compute = [&](auto buf, int kt) {

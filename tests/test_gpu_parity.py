@@ -43,12 +43,25 @@ def _L():
 # packing
 # ----------------------------------------------------------------------------
 def _unpack_experts(buf: np.ndarray, G, K, N, S, elem_bytes, KF):
-    """Inverse of the fragment layout, written from its definition."""
+    """Inverse of the packed layout, written from its definition: per matrix,
+    blocks of up to 8 fragment columns (16 columns each); inside a block the
+    order is step kt, plane s, fragment j; a fragment holds lane q*16 + r
+    (column r, reduction elements q*KF/4 + i)."""
     per = KF // 4
     dt = {4: np.float32, 2: np.uint16, 1: np.int8}[elem_bytes]
-    a = buf.view(dt).reshape(G, N // 16, K // KF, S, 4, 16, per)     # g nt kt s q r i
-    a = a.transpose(0, 3, 2, 4, 6, 1, 5)                              # g s kt q i nt r
-    return a.reshape(G, S, K, N)
+    NT, KT = N // 16, K // KF
+    flat = buf.view(dt).reshape(G, -1)
+    out = np.empty((G, S, K, N), dtype=dt)
+    pos = 0
+    for cb in range(0, NT, 8):
+        w = min(8, NT - cb)
+        n = KT * S * w * 64 * per
+        blk = flat[:, pos:pos + n].reshape(G, KT, S, w, 4, 16, per)   # g kt s j q r i
+        blk = blk.transpose(0, 2, 1, 4, 6, 3, 5)                       # g s kt q i j r
+        out[:, :, :, cb * 16:(cb + w) * 16] = blk.reshape(G, S, K, w * 16)
+        pos += n
+    assert pos == flat.shape[1]
+    return out
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16", "w8a8"])
