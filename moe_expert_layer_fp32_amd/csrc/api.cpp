@@ -60,6 +60,7 @@ GemmElem router_elem(const moe_desc* d) { return d->dtype == MOE_DTYPE_F32 ? ELE
 // ---------------------------------------------------------------------------
 constexpr int PREFILL_T = 1024;
 constexpr int TARGET_WGS = 256;
+constexpr int MAX_DENSE_SPLITS = 32;  // split-K of dense products (partials added in split order)
 constexpr int PERSISTENT_WGS = 512;   // grid cap of the tiled kernel (it loops over tiles)
 
 struct DensePlan {
@@ -86,7 +87,7 @@ DensePlan plan_dense(int M, int N, int K, GemmElem el, int nacc) {
   const int wgs = ceil_div(N, 4 * L.wave_features) * mt;
   const int kc = K / ch;
   int splits = 1;
-  if (wgs < TARGET_WGS) splits = std::max(1, std::min({ceil_div(TARGET_WGS, wgs), kc / 2, 8}));
+  if (wgs < TARGET_WGS) splits = std::max(1, std::min({ceil_div(TARGET_WGS, wgs), kc / 2, MAX_DENSE_SPLITS}));
   L.splits = splits;
   L.min_rows = 0;
   L.max_rows = INT32_MAX;
@@ -99,6 +100,28 @@ DensePlan plan_dense(int M, int N, int K, GemmElem el, int nacc) {
 
 bool routed_tiled(const moe_desc* d, int N, int K) {
   return K % lds_chunk_elems(weight_elem(d)) == 0 && N % 32 == 0;
+}
+
+// Decode-sized routed products with too few tiles to fill the device (e.g.
+// 8 resident experts: 8 x 16 column blocks of 128) split the reduction over
+// several workgroups per tile, up to SPLIT_WGS workgroups in all; the partial
+// sums are added in split order by the reduce pass. 1 = no split.
+constexpr int SPLIT_WGS = 512;
+int routed_splits(const moe_desc* d, int N, int K) {
+  if (d->T >= PREFILL_T || !routed_tiled(d, N, K)) return 1;
+  const long wgs = long(d->n_ffn) * ceil_div(N, 128);
+  if (wgs >= TARGET_WGS) return 1;
+  const int kc = K / lds_chunk_elems(weight_elem(d));
+  return std::max(1, std::min({int(ceil_div(SPLIT_WGS, int(wgs))), kc / 2, 8}));
+}
+// Split-K partial sums of the routed products (the larger of the two).
+size_t routed_partial_bytes(const moe_desc* d) {
+  if (d->n_ffn == 0) return 0;
+  size_t b = 0;
+  const int s1 = routed_splits(d, d->inter, d->d), s2 = routed_splits(d, d->d, d->inter);
+  if (s1 > 1) b = std::max(b, size_t(s1) * r_max(d) * 2 * d->inter * 4);
+  if (s2 > 1) b = std::max(b, size_t(s2) * r_max(d) * 1 * d->d * 4);
+  return b;
 }
 
 // Split-K partial sums needed by any dense product of this layer.
@@ -209,6 +232,7 @@ LayerWs carve_layer(Carve& c, const moe_desc* d) {
   L.shared.qx = L.routed.qx;
   L.shared.sx = L.routed.sx;
   carve_h(c, d, r_max(d), d->inter, L.routed);
+  L.routed.partial = c.take(routed_partial_bytes(d));
   L.rows = static_cast<float*>(c.take(size_t(r_max(d)) * d->d * 4));
   if (d->shared_inter > 0) {
     carve_h(c, d, d->T, d->shared_inter, L.shared);
@@ -247,10 +271,26 @@ moe_status run_dense(GemmArgs g, int M, GemmElem el, int planes, GemmEpi epi, vo
 // several); from PREFILL_T tokens up, experts with at most 64 rows use
 // 64-row tiles and bigger ones 128-row tiles (each weight fragment reused by
 // more rows). Few experts with long rows (fewer than TARGET_WGS tiled
-// workgroups, e.g. 8 resident experts of d 7168) and shapes that do not tile
-// stream through gemm_rows_kernel, whose wavefronts split the reduction.
-moe_status run_routed(GemmArgs g, const moe_desc* d, GemmElem el, int planes, GemmEpi epi, hipStream_t s,
-                      KernelEvents ev = {}) {
+// workgroups, e.g. 8 resident experts of d 7168) split the reduction over
+// workgroups (routed_splits); shapes that do not tile stream through
+// gemm_rows_kernel, whose wavefronts split the reduction.
+moe_status run_routed(GemmArgs g, const moe_desc* d, GemmElem el, int planes, GemmEpi epi, void* partial,
+                      hipStream_t s, KernelEvents ev = {}) {
+  const int splits = routed_splits(d, g.N, g.K);
+  if (splits > 1) {
+    LdsArgs L{};
+    L.wave_features = 32;
+    L.splits = splits;
+    L.partial = partial;
+    L.part_rows = r_max(d);
+    L.max_wgs = PERSISTENT_WGS;
+    L.tile_rows = 64;
+    L.min_rows = 1;
+    L.max_rows = INT32_MAX;
+    g.tiles_y = ceil_div(r_max(d), L.tile_rows) + g.n_groups;
+    HIP_TRY(launch_gemm_lds(g, L, el, planes, epi, s, ev));
+    return MOE_OK;
+  }
   const long tiled_wgs = long(g.n_groups) * ceil_div(g.N, 128);
   if (routed_tiled(d, g.N, g.K) && (tiled_wgs >= TARGET_WGS || d->T >= PREFILL_T)) {
     LdsArgs L{};
@@ -389,7 +429,7 @@ moe_status run_ffn(const moe_desc* d, const FfnPlan& p, const void* x, const Ffn
   g1.ldo = size_t(p.inter) * h_bytes(d);
   g1.out_bf16 = d->dtype == MOE_DTYPE_BF16;
   const KernelEvents ev1{e1b, e1e}, ev2{e2b, e2e};
-  st = routed ? run_routed(g1, d, el, 2, EPI_SWIGLU, s, ev1)
+  st = routed ? run_routed(g1, d, el, 2, EPI_SWIGLU, f.partial, s, ev1)
               : run_dense(g1, d->T, el, 2, EPI_SWIGLU, f.partial, s, ev1);
   if (st != MOE_OK) return st;
 
@@ -415,7 +455,7 @@ moe_status run_ffn(const moe_desc* d, const FfnPlan& p, const void* x, const Ffn
   g2.out = reinterpret_cast<uint8_t*>(rows);
   g2.ldo = size_t(d->d) * 4;
   g2.out_bf16 = 0;
-  st = routed ? run_routed(g2, d, el, 1, EPI_SUM, s, ev2)
+  st = routed ? run_routed(g2, d, el, 1, EPI_SUM, f.partial, s, ev2)
               : run_dense(g2, d->T, el, 1, EPI_SUM, f.partial, s, ev2);
   if (st != MOE_OK) return st;
   return MOE_OK;
@@ -473,6 +513,7 @@ size_t ws_bytes_of(const moe_desc* d, int op) {
       FfnWs f{};
       carve_qx(c, d, f);
       carve_h(c, d, r_max(d), d->inter, f);
+      c.take(routed_partial_bytes(d));
       break;
     }
     case MOE_OP_FFN_SHARED: {
@@ -595,7 +636,7 @@ moe_status moe_grouped_ffn(const moe_desc* d, const moe_weights* w, int which, c
   FfnWs f{};
   carve_qx(c, d, f);
   carve_h(c, d, routed ? r_max(d) : d->T, routed ? d->inter : d->shared_inter, f);
-  if (!routed) f.partial = c.take(dense_partial_bytes(d, false, true));
+  f.partial = c.take(routed ? routed_partial_bytes(d) : dense_partial_bytes(d, false, true));
   if (w8a8(d)) {
     st = run_quant_x(d, x, f, s);
     if (st != MOE_OK) return st;

@@ -363,7 +363,7 @@ __device__ __forceinline__ void gemm_lds_tile(const GemmArgs& a, const LdsArgs& 
 // workgroups on that XCD. Tiles sharing a weight column block thus run close
 // together in time on one L2.
 template <class Tr, int S, int EPI, int NF, int BM>
-constexpr int ring_steps() { return S == 1 ? 8 : 4; }
+constexpr int ring_steps() { return S == 1 || BM == 128 ? 8 : 4; }
 template <class Tr, int S, int EPI, int NF, int BM>
 constexpr int lds_waves_per_eu() { return BM == 64 && NF == 32 && ring_steps<Tr, S, EPI, NF, BM>() <= 8 ? 2 : 1; }
 
@@ -399,62 +399,67 @@ template <typename PT, int EPI>
 __global__ __launch_bounds__(256) void gemm_reduce_kernel(GemmArgs a, LdsArgs L) {
   constexpr int NACC = (EPI == EPI_SWIGLU) ? 2 : 1;
   const int cols4 = a.N / 4;
-  const size_t idx = blockIdx.x * size_t(blockDim.x) + threadIdx.x;
-  const int orow = int(idx / cols4);
-  const int c0 = int(idx % cols4) * 4;
-  if (orow >= L.part_rows) return;
-  // Which group holds this compacted row, and is it one this product covered?
-  int g = 0, brow = orow;
+  // Rows to reduce: the compacted rows of the groups (known on the device
+  // only), or the dense rows; a grid-stride loop covers them.
+  int base = 0, rows = min(a.dense_rows, L.part_rows);
   if (a.offsets) {
-    const int base = a.offsets[a.first];
-    const int srow = orow + base;
-    if (srow >= a.offsets[a.first + a.n_groups]) return;
-    int lo = 0, hi = a.n_groups - 1;   // last group whose start <= srow
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) / 2;
-      if (a.offsets[a.first + mid] <= srow) lo = mid; else hi = mid - 1;
-    }
-    g = lo;
-    const int n = a.offsets[a.first + g + 1] - a.offsets[a.first + g];
-    if (n < L.min_rows || n > L.max_rows) return;
-    brow = a.sorted_slot ? a.sorted_slot[srow] / a.k : orow;
-  } else if (orow >= a.dense_rows) {
-    return;
+    base = a.offsets[a.first];
+    rows = min(a.offsets[a.first + a.n_groups] - base, L.part_rows);
   }
-  float sum[NACC][4];
-#pragma unroll
-  for (int s = 0; s < NACC; ++s) {
-    PT t[4] = {0, 0, 0, 0};
-    for (int sp = 0; sp < L.splits; ++sp) {
-      const PT* P = reinterpret_cast<const PT*>(L.partial) + (size_t(sp) * L.part_rows + orow) * size_t(NACC) * a.N +
-                    size_t(s) * a.N + c0;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) t[j] += P[j];
+  const size_t total = size_t(rows) * cols4;
+  for (size_t idx = blockIdx.x * size_t(blockDim.x) + threadIdx.x; idx < total;
+       idx += size_t(gridDim.x) * blockDim.x) {
+    const int orow = int(idx / cols4);
+    const int c0 = int(idx % cols4) * 4;
+    // Which group holds this compacted row, and is it one this product covered?
+    int g = 0, brow = orow;
+    if (a.offsets) {
+      const int srow = orow + base;
+      int lo = 0, hi = a.n_groups - 1;   // last group whose start <= srow
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) / 2;
+        if (a.offsets[a.first + mid] <= srow) lo = mid; else hi = mid - 1;
+      }
+      g = lo;
+      const int n = a.offsets[a.first + g + 1] - a.offsets[a.first + g];
+      if (n < L.min_rows || n > L.max_rows) continue;
+      brow = a.sorted_slot ? a.sorted_slot[srow] / a.k : orow;
     }
+    float sum[NACC][4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) sum[s][j] = float(t[j]);
-  }
-  const float bs = a.b_scale ? a.b_scale[brow] : 1.f;
-  float v[4];
+    for (int s = 0; s < NACC; ++s) {
+      PT t[4] = {0, 0, 0, 0};
+      for (int sp = 0; sp < L.splits; ++sp) {
+        const PT* P = reinterpret_cast<const PT*>(L.partial) + (size_t(sp) * L.part_rows + orow) * size_t(NACC) * a.N +
+                      size_t(s) * a.N + c0;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const float cs0 = a.a_scale0 ? a.a_scale0[size_t(g) * a.a_scale_stride + c0 + j] : 1.f;
-    if (EPI == EPI_SWIGLU) {
-      const float cs1 = a.a_scale1 ? a.a_scale1[size_t(g) * a.a_scale_stride + c0 + j] : 1.f;
-      v[j] = silu_f(sum[0][j] * bs * cs0) * (sum[1][j] * bs * cs1);
+        for (int j = 0; j < 4; ++j) t[j] += P[j];
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) sum[s][j] = float(t[j]);
+    }
+    const float bs = a.b_scale ? a.b_scale[brow] : 1.f;
+    float v[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float cs0 = a.a_scale0 ? a.a_scale0[size_t(g) * a.a_scale_stride + c0 + j] : 1.f;
+      if (EPI == EPI_SWIGLU) {
+        const float cs1 = a.a_scale1 ? a.a_scale1[size_t(g) * a.a_scale_stride + c0 + j] : 1.f;
+        v[j] = silu_f(sum[0][j] * bs * cs0) * (sum[1][j] * bs * cs1);
+      } else {
+        const float bias = (a.bias && c0 + j < a.n_valid) ? a.bias[c0 + j] : 0.f;
+        v[j] = sum[0][j] * bs * cs0 + bias;
+      }
+    }
+    uint8_t* op = a.out + size_t(orow) * a.ldo;
+    if (a.out_bf16) {
+      u32x2 pk;
+      pk[0] = uint32_t(f32_to_bf16(v[0])) | (uint32_t(f32_to_bf16(v[1])) << 16);
+      pk[1] = uint32_t(f32_to_bf16(v[2])) | (uint32_t(f32_to_bf16(v[3])) << 16);
+      *reinterpret_cast<u32x2*>(op + size_t(c0) * 2) = pk;
     } else {
-      const float bias = (a.bias && c0 + j < a.n_valid) ? a.bias[c0 + j] : 0.f;
-      v[j] = sum[0][j] * bs * cs0 + bias;
+      *reinterpret_cast<f32x4*>(op + size_t(c0) * 4) = f32x4{v[0], v[1], v[2], v[3]};
     }
-  }
-  uint8_t* op = a.out + size_t(orow) * a.ldo;
-  if (a.out_bf16) {
-    u32x2 pk;
-    pk[0] = uint32_t(f32_to_bf16(v[0])) | (uint32_t(f32_to_bf16(v[1])) << 16);
-    pk[1] = uint32_t(f32_to_bf16(v[2])) | (uint32_t(f32_to_bf16(v[3])) << 16);
-    *reinterpret_cast<u32x2*>(op + size_t(c0) * 2) = pk;
-  } else {
-    *reinterpret_cast<f32x4*>(op + size_t(c0) * 4) = f32x4{v[0], v[1], v[2], v[3]};
   }
 }
 
@@ -471,8 +476,9 @@ static hipError_t launch_lds_one(const GemmArgs& a, const LdsArgs& L, hipStream_
                               reduce ? nullptr : ev.stop, a, L);
   if (e != hipSuccess || !reduce) return e;
   const size_t threads = size_t(L.part_rows) * (a.N / 4);
-  return launch_timed((gemm_reduce_kernel<typename Tr::part_t, EPI>), dim3(unsigned((threads + 255) / 256)),
-                      dim3(256), stream, nullptr, ev.stop, a, L);
+  const unsigned blocks = unsigned(std::min<size_t>((threads + 255) / 256, 2048));   // grid-stride beyond
+  return launch_timed((gemm_reduce_kernel<typename Tr::part_t, EPI>), dim3(blocks), dim3(256), stream, nullptr,
+                      ev.stop, a, L);
 }
 
 // Products with two or three weight planes always use 32 features per

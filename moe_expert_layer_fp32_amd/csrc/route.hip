@@ -31,6 +31,7 @@ namespace moe {
 constexpr int ROW = 16;            // lanes per token
 constexpr int GATE_TOKENS = WAVE / ROW;
 constexpr int GROUP_SLOTS = 4;     // group-limited routing: n_group <= 64
+constexpr int GATE_SPLIT_BATCH = 4;  // split-K partial sums loaded together
 
 __device__ inline uint32_t order_bits(float f) {
   const uint32_t b = __float_as_uint(f + 0.0f);   // -0 -> +0
@@ -96,10 +97,17 @@ __device__ inline void merge_top2_dpp(float& t1, float& t2) {
   merge_top2(t1, t2, b1, b2);
 }
 
-template <int PL>
-__global__ __launch_bounds__(WAVE) void gate_topk_kernel(GateArgs a) {
+// FW wavefronts per workgroup. With split-K partial sums FW > 1: wavefront w
+// adds splits w, w + FW, ... (in that order) for the workgroup's four tokens,
+// the FW sums meet in LDS and are added in wavefront order; every wavefront
+// then runs the same gate on the same tokens (no wavefront leaves before the
+// last barrier) and only the first writes the result.
+template <int PL, int FW>
+__global__ __launch_bounds__(FW * WAVE) void gate_topk_kernel(GateArgs a) {
   __shared__ float sc_lds[GATE_TOKENS][PL * ROW];
-  const int lane = threadIdx.x;
+  __shared__ float fold[FW][GATE_TOKENS][PL * ROW];
+  const int lane = threadIdx.x & (WAVE - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / WAVE);
   const int r = lane & (ROW - 1), row = lane / ROW;
   const int t_raw = blockIdx.x * GATE_TOKENS + row;
   const bool live = t_raw < a.T;            // dead rows work on a valid token and write nothing
@@ -120,11 +128,35 @@ __global__ __launch_bounds__(WAVE) void gate_topk_kernel(GateArgs a) {
     for (int i = 0; i < PL; ++i)
       if (valid[i]) u[i] = a.z[size_t(t) * a.ldz + i * ROW + r];
   } else {
-    for (int sp = 0; sp < a.splits; ++sp) {
-      const float* P = a.partial + (size_t(sp) * a.T + t) * a.ldz + r;
+    // This wavefront's splits, GATE_SPLIT_BATCH loads at a time (clamped
+    // split index: every address is valid; absent splits add +0).
+    float mine[PL];
 #pragma unroll
-      for (int i = 0; i < PL; ++i)
-        if (valid[i]) u[i] += P[i * ROW];
+    for (int i = 0; i < PL; ++i) mine[i] = 0.f;
+    for (int sp0 = wave; sp0 < a.splits; sp0 += GATE_SPLIT_BATCH * FW) {
+      float part[GATE_SPLIT_BATCH][PL];
+#pragma unroll
+      for (int q = 0; q < GATE_SPLIT_BATCH; ++q) {
+        const float* P = a.partial + (size_t(min(sp0 + q * FW, a.splits - 1)) * a.T + t) * a.ldz + r;
+#pragma unroll
+        for (int i = 0; i < PL; ++i) part[q][i] = P[min(i * ROW, a.ldz - ROW)];
+      }
+#pragma unroll
+      for (int q = 0; q < GATE_SPLIT_BATCH; ++q)
+#pragma unroll
+        for (int i = 0; i < PL; ++i) mine[i] += (sp0 + q * FW < a.splits && valid[i]) ? part[q][i] : 0.f;
+    }
+    if (FW == 1) {
+#pragma unroll
+      for (int i = 0; i < PL; ++i) u[i] = mine[i];
+    } else {
+#pragma unroll
+      for (int i = 0; i < PL; ++i) fold[wave][row][i * ROW + r] = mine[i];
+      __syncthreads();
+#pragma unroll
+      for (int w = 0; w < FW; ++w)
+#pragma unroll
+        for (int i = 0; i < PL; ++i) u[i] += fold[w][row][i * ROW + r];
     }
     if (a.bias) {
 #pragma unroll
@@ -236,7 +268,7 @@ __global__ __launch_bounds__(WAVE) void gate_topk_kernel(GateArgs a) {
   const bool mine = r < a.k && sel_e >= 0;
   const float s = mine ? sc_lds[row][sel_e] : 0.f;
   const float total = row_sum_f32(s);
-  if (live && r < a.k) {
+  if (wave == 0 && live && r < a.k) {
     float wv = a.renorm ? s / total : s;
     wv *= a.route_scale;
     a.topk_idx[size_t(t) * a.k + r] = sel_e;
@@ -244,18 +276,30 @@ __global__ __launch_bounds__(WAVE) void gate_topk_kernel(GateArgs a) {
   }
 }
 
+constexpr int GATE_FOLD_WAVES = 8;
+template <int PL>
+static hipError_t launch_gate_pl(const GateArgs& a, hipStream_t stream) {
+  const dim3 grid(ceil_div(a.T, GATE_TOKENS));
+  // Folding over several wavefronts pays for few tokens with many splits;
+  // for many tokens the redundant gate work of the extra wavefronts costs more.
+  if (a.partial && a.splits > 2 && a.T <= 2048)
+    hipLaunchKernelGGL((gate_topk_kernel<PL, GATE_FOLD_WAVES>), grid, dim3(GATE_FOLD_WAVES * WAVE), 0, stream, a);
+  else
+    hipLaunchKernelGGL((gate_topk_kernel<PL, 1>), grid, dim3(WAVE), 0, stream, a);
+  return hipGetLastError();
+}
+
 hipError_t launch_gate(const GateArgs& a, hipStream_t stream) {
   if (a.T <= 0) return hipSuccess;
-  const dim3 grid(ceil_div(a.T, GATE_TOKENS)), block(WAVE);
+  if (a.partial && a.splits < 1) return hipErrorInvalidValue;
   const int pl = ceil_div(a.E, ROW);
-  if (pl <= 1) hipLaunchKernelGGL(gate_topk_kernel<1>, grid, block, 0, stream, a);
-  else if (pl <= 2) hipLaunchKernelGGL(gate_topk_kernel<2>, grid, block, 0, stream, a);
-  else if (pl <= 4) hipLaunchKernelGGL(gate_topk_kernel<4>, grid, block, 0, stream, a);
-  else if (pl <= 6) hipLaunchKernelGGL(gate_topk_kernel<6>, grid, block, 0, stream, a);
-  else if (pl <= 8) hipLaunchKernelGGL(gate_topk_kernel<8>, grid, block, 0, stream, a);
-  else if (pl <= 12) hipLaunchKernelGGL(gate_topk_kernel<12>, grid, block, 0, stream, a);
-  else hipLaunchKernelGGL(gate_topk_kernel<16>, grid, block, 0, stream, a);
-  return hipGetLastError();
+  if (pl <= 1) return launch_gate_pl<1>(a, stream);
+  if (pl <= 2) return launch_gate_pl<2>(a, stream);
+  if (pl <= 4) return launch_gate_pl<4>(a, stream);
+  if (pl <= 6) return launch_gate_pl<6>(a, stream);
+  if (pl <= 8) return launch_gate_pl<8>(a, stream);
+  if (pl <= 12) return launch_gate_pl<12>(a, stream);
+  return launch_gate_pl<16>(a, stream);
 }
 
 // ---------------------------------------------------------------------------
