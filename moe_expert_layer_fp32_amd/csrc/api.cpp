@@ -211,9 +211,15 @@ void carve_h(Carve& c, const moe_desc* d, int rows, int inter, FfnWs& f) {
   f.partial = nullptr;
 }
 
+size_t permute_ws_bytes(const moe_desc* d) {
+  const int chunks = permute_chunks(d->T * d->k);
+  return chunks > 1 ? size_t(chunks) * d->E * 4 : 0;
+}
+
 struct LayerWs {
   RouteWs route;
   int32_t *idx, *counts, *offsets, *sorted_slot, *slot_pos;
+  int32_t* chunk_hist;
   float* w;
   FfnWs routed, shared;
   float *rows, *shared_rows;
@@ -228,6 +234,7 @@ LayerWs carve_layer(Carve& c, const moe_desc* d) {
   L.offsets = static_cast<int32_t*>(c.take(size_t(d->E + 1) * 4));
   L.sorted_slot = static_cast<int32_t*>(c.take(slots * 4));
   L.slot_pos = static_cast<int32_t*>(c.take(slots * 4));
+  L.chunk_hist = static_cast<int32_t*>(c.take(permute_ws_bytes(d)));
   carve_qx(c, d, L.routed);
   L.shared.qx = L.routed.qx;
   L.shared.sx = L.routed.sx;
@@ -508,7 +515,7 @@ size_t ws_bytes_of(const moe_desc* d, int op) {
   Carve c(nullptr);
   switch (op) {
     case MOE_OP_ROUTE_TOPK: carve_route(c, d); break;
-    case MOE_OP_PERMUTE: break;
+    case MOE_OP_PERMUTE: c.take(permute_ws_bytes(d)); break;
     case MOE_OP_FFN_ROUTED: {
       FfnWs f{};
       carve_qx(c, d, f);
@@ -605,14 +612,14 @@ moe_status moe_route_topk(const moe_desc* d, const moe_weights* w, const void* x
 
 moe_status moe_permute(const moe_desc* d, const int32_t* topk_idx, int32_t* counts, int32_t* offsets,
                        int32_t* sorted_slot, int32_t* slot_pos, void* ws, size_t ws_bytes, void* stream) {
-  (void)ws;
-  (void)ws_bytes;
   moe_status st = validate(d);
   if (st != MOE_OK) return st;
   if (!counts || !offsets) return MOE_ERR_INVALID_ARG;
   if (d->T > 0 && (!topk_idx || !sorted_slot || !slot_pos)) return MOE_ERR_INVALID_ARG;
+  const size_t need = permute_ws_bytes(d);
+  if (need > 0 && (ws_bytes < need || !ws)) return MOE_ERR_WORKSPACE;
   return launch_permute(topk_idx, d->T * d->k, d->E, counts, offsets, sorted_slot, slot_pos,
-                        static_cast<hipStream_t>(stream)) == hipSuccess
+                        static_cast<int32_t*>(ws), static_cast<hipStream_t>(stream)) == hipSuccess
              ? MOE_OK
              : MOE_ERR_HIP;
 }
@@ -705,7 +712,7 @@ moe_status moe_layer(const moe_desc* d, const moe_weights* w, const void* x, voi
     st = run_route(d, w, x, idx, tw, L.route, s);
     if (st != MOE_OK) return st;
   }
-  HIP_TRY(launch_permute(idx, d->T * d->k, d->E, counts, offsets, sorted_slot, slot_pos, s));
+  HIP_TRY(launch_permute(idx, d->T * d->k, d->E, counts, offsets, sorted_slot, slot_pos, L.chunk_hist, s));
   if (d->T == 0) return MOE_OK;
   if (d->n_ffn > 0) {
     st = run_ffn(d, routed_plan(d, w, offsets, sorted_slot), x, L.routed, L.rows, s,

@@ -25,11 +25,10 @@
 
 #include "common.h"
 #include "kernels.h"
+#include "tiles.h"
 
 namespace moe {
 
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef int i32x16 __attribute__((ext_vector_type(16)));
 
 struct M32BF16 {
   using op_t = bf16x8;
@@ -68,88 +67,6 @@ struct M32F32 {
 
 constexpr int CH_BYTES = 256;              // bytes of one row per LDS chunk
 constexpr int LDS_ROW = CH_BYTES + 16;     // padded row stride (4-bank shift per row)
-
-__device__ inline float silu_f(float v) { return v / (1.0f + expf(-v)); }
-
-// Locate m-tile `tile` (rows per tile `tm`) among the groups whose row count
-// lies in [lo, hi]. Wave-uniform; false past the last tile.
-__device__ inline bool locate_tile_lds(const GemmArgs& a, int tile, int tm, int lo, int hi, int& g, int& row0,
-                                       int& nrows, int& out0) {
-  if (a.offsets == nullptr) {
-    g = 0;
-    row0 = tile * tm;
-    nrows = min(tm, a.dense_rows - row0);
-    out0 = row0;
-    return nrows > 0;
-  }
-  const int lane = threadIdx.x & (WAVE - 1);
-  const int base = a.offsets[a.first];
-  int cnt[4];
-  int local = 0;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int gg = lane * 4 + i;
-    int c = 0;
-    if (gg < a.n_groups) {
-      const int n = a.offsets[a.first + gg + 1] - a.offsets[a.first + gg];
-      if (n >= lo && n <= hi) c = ceil_div(n, tm);
-    }
-    cnt[i] = c;
-    local += c;
-  }
-  int incl = local;
-#pragma unroll
-  for (int d = 1; d < WAVE; d <<= 1) {
-    const int v = __shfl_up(incl, d, WAVE);
-    if (lane >= d) incl += v;
-  }
-  const int excl = incl - local;
-  const uint64_t hit = __ballot(tile >= excl && tile < incl);
-  if (hit == 0) return false;
-  const int src = __builtin_ctzll(hit);
-  int my_g = -1, my_mt = 0;
-  if (lane == src) {
-    int t = tile - excl;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      if (my_g < 0) {
-        if (t < cnt[i]) {
-          my_g = lane * 4 + i;
-          my_mt = t;
-        } else {
-          t -= cnt[i];
-        }
-      }
-    }
-  }
-  g = __shfl(my_g, src, WAVE);
-  const int mt = __shfl(my_mt, src, WAVE);
-  const int gbeg = a.offsets[a.first + g];
-  const int gend = a.offsets[a.first + g + 1];
-  row0 = gbeg + mt * tm;
-  nrows = min(tm, gend - row0);
-  out0 = row0 - base;
-  return true;
-}
-
-// Number of m-tiles (rows per tile tm) among the groups whose row count lies
-// in [lo, hi]; dense: ceil(rows / tm). Wave-uniform.
-__device__ inline int count_tiles_lds(const GemmArgs& a, int tm, int lo, int hi) {
-  if (a.offsets == nullptr) return ceil_div(a.dense_rows, tm);
-  const int lane = threadIdx.x & (WAVE - 1);
-  int local = 0;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int gg = lane * 4 + i;
-    if (gg < a.n_groups) {
-      const int n = a.offsets[a.first + gg + 1] - a.offsets[a.first + gg];
-      if (n >= lo && n <= hi) local += ceil_div(n, tm);
-    }
-  }
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) local += __shfl_xor(local, o, WAVE);
-  return local;
-}
 
 template <class Tr, int S, int EPI, int NF, int BM, int RA>
 __device__ __forceinline__ void gemm_lds_tile(const GemmArgs& a, const LdsArgs& L, uint8_t (&lds)[2][BM * LDS_ROW],
@@ -463,6 +380,17 @@ __global__ __launch_bounds__(256) void gemm_reduce_kernel(GemmArgs a, LdsArgs L)
   }
 }
 
+hipError_t launch_gemm_reduce(const GemmArgs& a, const LdsArgs& L, GemmElem elem, GemmEpi epi, hipStream_t stream,
+                              hipEvent_t stop) {
+  const size_t threads = size_t(L.part_rows) * (a.N / 4);
+  const dim3 grid(unsigned(std::min<size_t>((threads + 255) / 256, 2048)));   // grid-stride beyond
+  if (elem == ELEM_I8)
+    return epi == EPI_SWIGLU ? launch_timed((gemm_reduce_kernel<int, EPI_SWIGLU>), grid, dim3(256), stream, nullptr, stop, a, L)
+                             : launch_timed((gemm_reduce_kernel<int, EPI_SUM>), grid, dim3(256), stream, nullptr, stop, a, L);
+  return epi == EPI_SWIGLU ? launch_timed((gemm_reduce_kernel<float, EPI_SWIGLU>), grid, dim3(256), stream, nullptr, stop, a, L)
+                           : launch_timed((gemm_reduce_kernel<float, EPI_SUM>), grid, dim3(256), stream, nullptr, stop, a, L);
+}
+
 int lds_chunk_elems(GemmElem elem) { return CH_BYTES / (elem == ELEM_F32 ? 4 : (elem == ELEM_BF16 ? 2 : 1)); }
 
 template <class Tr, int S, int EPI, int NF, int BM>
@@ -475,10 +403,8 @@ static hipError_t launch_lds_one(const GemmArgs& a, const LdsArgs& L, hipStream_
   hipError_t e = launch_timed((gemm_lds_kernel<Tr, S, EPI, NF, BM>), grid, dim3(WG_THREADS), stream, ev.start,
                               reduce ? nullptr : ev.stop, a, L);
   if (e != hipSuccess || !reduce) return e;
-  const size_t threads = size_t(L.part_rows) * (a.N / 4);
-  const unsigned blocks = unsigned(std::min<size_t>((threads + 255) / 256, 2048));   // grid-stride beyond
-  return launch_timed((gemm_reduce_kernel<typename Tr::part_t, EPI>), dim3(blocks), dim3(256), stream, nullptr,
-                      ev.stop, a, L);
+  return launch_gemm_reduce(a, L, std::is_same<typename Tr::part_t, int>::value ? ELEM_I8 : ELEM_BF16, GemmEpi(EPI),
+                            stream, ev.stop);
 }
 
 // Products with two or three weight planes always use 32 features per

@@ -92,6 +92,10 @@ struct LdsArgs {
 hipError_t launch_gemm_lds(const GemmArgs& a, const LdsArgs& L, GemmElem elem, int planes, GemmEpi epi,
                            hipStream_t stream, KernelEvents ev = {});
 int lds_chunk_elems(GemmElem elem);
+// Reduce pass of a split product: partial sums added in split order, then
+// the product's epilogue (stop: optional timing event stamped at its end).
+hipError_t launch_gemm_reduce(const GemmArgs& a, const LdsArgs& L, GemmElem elem, GemmEpi epi, hipStream_t stream,
+                              hipEvent_t stop);
 
 // ---------------------------------------------------------------------------
 // Gating + top-k (route.hip)
@@ -124,8 +128,13 @@ hipError_t launch_router_small(const RouterArgs& a, bool f32, hipStream_t stream
 // ---------------------------------------------------------------------------
 // Stable counting sort of slots by expert (permute.hip)
 // ---------------------------------------------------------------------------
+// Slots per workgroup of the multi-workgroup permutation (more slots than
+// this use permute_chunks(n) workgroups and a chunk_hist workspace of
+// permute_chunks(n) * E ints; fewer use one workgroup and no workspace).
+constexpr int PERMUTE_CHUNK = 8192;
+int permute_chunks(int n_slots);
 hipError_t launch_permute(const int* topk_idx, int n_slots, int E, int* counts, int* offsets,
-                          int* sorted_slot, int* slot_pos, hipStream_t stream);
+                          int* sorted_slot, int* slot_pos, int* chunk_hist, hipStream_t stream);
 
 // ---------------------------------------------------------------------------
 // Per-row int8 quantisation (quant.hip). rows = fixed count, or (when

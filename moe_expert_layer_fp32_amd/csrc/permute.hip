@@ -17,6 +17,13 @@
 //     the group size. Slots of one expert therefore keep ascending slot
 //     order (stable), which fixes the permutation uniquely.
 // Ids outside [0, E) are not counted; their slot_pos is -1.
+//
+// Many slots (prefill: T*k = 65536) spread the same steps over several
+// workgroups, each owning a contiguous chunk of slots: one pass histograms
+// every chunk into the workspace; a second pass gives each chunk its
+// starting position per expert (the expert's offset plus the counts of the
+// chunks before it, summed in chunk order) and places the chunk's slots as
+// above. The result is the same permutation, bit for bit.
 #include "common.h"
 #include "kernels.h"
 
@@ -26,7 +33,26 @@ constexpr int PERM_WAVES = 16;
 constexpr int PERM_THREADS = PERM_WAVES * WAVE;
 constexpr int PERM_MAX_E = 256;
 
+// Histogram of the chunk [chunk * blockIdx.x, ...) of each workgroup into
+// chunk_hist[blockIdx.x][E] (integer LDS atomics: order-independent).
+__global__ __launch_bounds__(PERM_THREADS) void permute_hist_kernel(const int* __restrict__ idx, int n, int E,
+                                                                    int chunk, int* __restrict__ chunk_hist) {
+  __shared__ int hist[PERM_MAX_E];
+  for (int i = threadIdx.x; i < PERM_MAX_E; i += PERM_THREADS) hist[i] = 0;
+  __syncthreads();
+  const int c0 = blockIdx.x * chunk, c1 = min(n, c0 + chunk);
+  for (int s = c0 + threadIdx.x; s < c1; s += PERM_THREADS) {
+    const int e = idx[s];
+    if (e >= 0 && e < E) atomicAdd(&hist[e], 1);
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += PERM_THREADS) chunk_hist[size_t(blockIdx.x) * E + e] = hist[e];
+}
+
+// Placement of the chunk of workgroup blockIdx.x (the whole range when
+// chunk_hist is null: one workgroup). Workgroup 0 writes counts and offsets.
 __global__ __launch_bounds__(PERM_THREADS) void permute_kernel(const int* __restrict__ idx, int n, int E,
+                                                               int chunk, const int* __restrict__ chunk_hist,
                                                                int* __restrict__ counts,
                                                                int* __restrict__ offsets,
                                                                int* __restrict__ sorted_slot,
@@ -35,14 +61,16 @@ __global__ __launch_bounds__(PERM_THREADS) void permute_kernel(const int* __rest
   __shared__ int expert_base[PERM_MAX_E + 1];
   const int lane = threadIdx.x & (WAVE - 1);
   const int wave = threadIdx.x / WAVE;
+  const int c0 = chunk_hist ? blockIdx.x * chunk : 0;
+  const int c1 = chunk_hist ? min(n, c0 + chunk) : n;
 
   for (int i = threadIdx.x; i < PERM_WAVES * PERM_MAX_E; i += PERM_THREADS) (&hist[0][0])[i] = 0;
   __syncthreads();
 
-  // Segment of this wave: [seg0, seg1), a multiple of 64 long.
-  const int seg_len = ceil_div(ceil_div(n, PERM_WAVES), WAVE) * WAVE;
-  const int seg0 = min(n, wave * seg_len);
-  const int seg1 = min(n, seg0 + seg_len);
+  // Segment of this wave inside the chunk: [seg0, seg1), a multiple of 64 long.
+  const int seg_len = ceil_div(ceil_div(c1 - c0, PERM_WAVES), WAVE) * WAVE;
+  const int seg0 = min(c1, c0 + wave * seg_len);
+  const int seg1 = min(c1, seg0 + seg_len);
 
   for (int s = seg0 + lane; s < seg1; s += WAVE) {
     const int e = idx[s];
@@ -50,16 +78,27 @@ __global__ __launch_bounds__(PERM_THREADS) void permute_kernel(const int* __rest
   }
   __syncthreads();
 
-  // Column prefix over waves (thread e), then exclusive scan over experts.
-  int total = 0;
+  // Column prefix over waves (thread e), then exclusive scan over experts of
+  // the expert totals (over all chunks); `before` = slots of expert e in the
+  // chunks ahead of this one.
+  int total = 0, before = 0;
   if (threadIdx.x < E) {
     const int e = threadIdx.x;
     for (int w = 0; w < PERM_WAVES; ++w) {
       const int c = hist[w][e];
-      hist[w][e] = total;     // exclusive prefix within the expert
+      hist[w][e] = total;     // exclusive prefix within the expert (this chunk)
       total += c;
     }
-    counts[e] = total;
+    if (chunk_hist) {
+      const int nchunks = ceil_div(n, chunk);
+      total = 0;
+      for (int b = 0; b < nchunks; ++b) {
+        const int c = chunk_hist[size_t(b) * E + e];
+        if (b < int(blockIdx.x)) before += c;
+        total += c;
+      }
+    }
+    if (blockIdx.x == 0) counts[e] = total;
   }
   // Scan totals over experts with wave 0..3 (E <= 256): simple two-level scan.
   __shared__ int wave_tot[PERM_MAX_E / WAVE];
@@ -81,10 +120,10 @@ __global__ __launch_bounds__(PERM_THREADS) void permute_kernel(const int* __rest
   }
   if (threadIdx.x == 0) expert_base[0] = 0;
   __syncthreads();
-  if (threadIdx.x <= E) offsets[threadIdx.x] = expert_base[threadIdx.x];
+  if (blockIdx.x == 0 && threadIdx.x <= E) offsets[threadIdx.x] = expert_base[threadIdx.x];
   if (threadIdx.x < E) {
     const int e = threadIdx.x;
-    for (int w = 0; w < PERM_WAVES; ++w) hist[w][e] += expert_base[e];   // segment start per expert
+    for (int w = 0; w < PERM_WAVES; ++w) hist[w][e] += expert_base[e] + before;   // segment start per expert
   }
   __syncthreads();
 
@@ -119,10 +158,21 @@ __global__ __launch_bounds__(PERM_THREADS) void permute_kernel(const int* __rest
   }
 }
 
+int permute_chunks(int n_slots) { return n_slots > PERMUTE_CHUNK ? ceil_div(n_slots, PERMUTE_CHUNK) : 1; }
+
 hipError_t launch_permute(const int* topk_idx, int n_slots, int E, int* counts, int* offsets,
-                          int* sorted_slot, int* slot_pos, hipStream_t stream) {
-  hipLaunchKernelGGL(permute_kernel, dim3(1), dim3(PERM_THREADS), 0, stream, topk_idx, n_slots, E,
-                     counts, offsets, sorted_slot, slot_pos);
+                          int* sorted_slot, int* slot_pos, int* chunk_hist, hipStream_t stream) {
+  const int nchunks = permute_chunks(n_slots);
+  if (nchunks == 1) {
+    hipLaunchKernelGGL(permute_kernel, dim3(1), dim3(PERM_THREADS), 0, stream, topk_idx, n_slots, E, n_slots,
+                       static_cast<const int*>(nullptr), counts, offsets, sorted_slot, slot_pos);
+    return hipGetLastError();
+  }
+  if (!chunk_hist) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(permute_hist_kernel, dim3(nchunks), dim3(PERM_THREADS), 0, stream, topk_idx, n_slots, E,
+                     PERMUTE_CHUNK, chunk_hist);
+  hipLaunchKernelGGL(permute_kernel, dim3(nchunks), dim3(PERM_THREADS), 0, stream, topk_idx, n_slots, E,
+                     PERMUTE_CHUNK, static_cast<const int*>(chunk_hist), counts, offsets, sorted_slot, slot_pos);
   return hipGetLastError();
 }
 

@@ -120,7 +120,7 @@ class DeviceLayer:
         offsets = torch.empty(self.cfg.E + 1, dtype=torch.int32, device=dev)
         ss = torch.empty(max(T * self.cfg.k, 1), dtype=torch.int32, device=dev)
         sp = torch.empty(max(T * self.cfg.k, 1), dtype=torch.int32, device=dev)
-        L.moe_permute(d, topk_idx, counts, offsets, ss, sp)
+        L.moe_permute(d, topk_idx, counts, offsets, ss, sp, self.workspace(L.OP_PERMUTE, T))
         return counts, offsets, ss, sp
 
     def grouped_ffn(self, which: int, offsets=None, sorted_slot=None, x=None):

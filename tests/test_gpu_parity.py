@@ -163,7 +163,8 @@ def _permute_case(T, k, E, seed, skew=0.0):
 
 
 PERMUTE_CASES = [(256, 8, 96, 1, 0.0), (512, 8, 256, 2, 0.0), (456, 8, 64, 3, 0.0), (8192, 8, 256, 4, 1.1),
-                 (1, 1, 1, 5, 0.0), (1, 16, 16, 6, 0.0), (333, 3, 7, 7, 2.0), (65536, 16, 256, 8, 1.1)]
+                 (1, 1, 1, 5, 0.0), (1, 16, 16, 6, 0.0), (333, 3, 7, 7, 2.0), (65536, 16, 256, 8, 1.1),
+                 (3000, 4, 32, 10, 0.0), (4096, 3, 3, 11, 1.5)]
 
 
 @pytest.mark.parametrize("T,k,E,seed,skew", PERMUTE_CASES)
@@ -177,15 +178,16 @@ def test_permute_bit_exact(T, k, E, seed, skew):
     offsets = torch.empty(E + 1, dtype=torch.int32, device="cuda")
     ss = torch.empty(T * k, dtype=torch.int32, device="cuda")
     sp = torch.empty(T * k, dtype=torch.int32, device="cuda")
-    L.moe_permute(d, ti, counts, offsets, ss, sp)
+    L.moe_permute(d, ti, counts, offsets, ss, sp, _permute_ws(L, d))
     want = O.routing_tables(idx, E)
     for got, ref, name in zip((counts, offsets, ss, sp), want, ("counts", "offsets", "sorted_slot", "slot_pos")):
         assert np.array_equal(U.np_of(got), ref), name
 
 
-def test_permute_all_tokens_on_one_expert_and_empty_experts():
+@pytest.mark.parametrize("T", [1000, 6000])   # one workgroup; three chunks
+def test_permute_all_tokens_on_one_expert_and_empty_experts(T):
     L, DeviceLayer, to_device = _L()
-    T, k, E = 1000, 3, 40
+    k, E = 3, 40
     idx = np.stack([np.array([7, 0, 39])] * T).astype(np.int32)
     cfg = MoEConfig(name="perm", T=T, d=64, E=E, k=k, gate="softmax", dtype="bf16")
     U.say("[gpu] permute skewed")
@@ -194,23 +196,31 @@ def test_permute_all_tokens_on_one_expert_and_empty_experts():
     assert all(np.array_equal(a, b) for a, b in zip((counts, offsets, ss, sp), want))
 
 
+def _permute_ws(L, d):
+    n = L.moe_workspace_bytes(d, L.OP_PERMUTE)
+    return torch.empty(n, dtype=torch.uint8, device="cuda") if n else None
+
+
 def _run_permute(L, cfg, idx):
     T, k, E = cfg.T, cfg.k, cfg.E
     ti = torch.from_numpy(np.ascontiguousarray(idx, dtype=np.int32)).cuda()
     out = [torch.empty(n, dtype=torch.int32, device="cuda") for n in (E, E + 1, T * k, T * k)]
-    L.moe_permute(L.desc_from_config(cfg), ti, *out)
+    d = L.desc_from_config(cfg)
+    L.moe_permute(d, ti, *out, _permute_ws(L, d))
     return [U.np_of(t) for t in out]
 
 
-def test_permute_drops_out_of_range_ids():
+@pytest.mark.parametrize("T,k", [(300, 4), (2500, 4)])   # one workgroup; several chunks (10000 slots)
+def test_permute_drops_out_of_range_ids(T, k):
     """Ids outside [0, E) are not counted and get slot_pos -1; the rest is the
     stable sort of the valid slots (library routine: numpy stable argsort)."""
     L, DeviceLayer, to_device = _L()
-    cfg, idx = _permute_case(300, 4, 32, 9)
+    cfg, idx = _permute_case(T, k, 32, 9)
     idx = idx.copy()
     idx[5, 1] = -1
     idx[17, 3] = 32
     idx[200, 0] = 1 << 20
+    idx[T - 1, k - 1] = -7
     U.say("[gpu] permute out-of-range ids")
     counts, offsets, ss, sp = _run_permute(L, cfg, idx)
     flat = idx.reshape(-1)
@@ -334,6 +344,34 @@ def test_combine(name):
     _, beyond = U.output_errors(U.np_of(y), want, cfg.dtype)
     assert beyond <= 1e-6
     del shared
+
+
+@pytest.mark.parametrize("T,skew", [(2048, 0.0), (2100, 1.5)])
+def test_grouped_ffn_large_tiles(T, skew):
+    """Many rows per weight: prefill-sized experts (hundreds of rows, 128-row
+    tiles, the skewed case mixing in 64-row tiles) and a dense shared expert
+    of 2048+ tokens with a split reduction (ragged token count)."""
+    L, DeviceLayer, to_device = _L()
+    cfg = MoEConfig(name="bigtile", T=T, d=512, E=8, k=2, gate="softmax", n_ffn=8, inter=256, shared_inter=512,
+                    dtype="bf16")
+    inp = make_inputs(cfg)
+    lay = DeviceLayer(cfg, inp)
+    idx, _ = make_routing(cfg, seed=5, skew=skew)
+    U.say(f"[gpu] large tiles T={T} skew={skew} counts={np.bincount(idx.ravel(), minlength=8).tolist()}")
+    counts, offsets, ss, sp = lay.permute(torch.from_numpy(idx).cuda())
+    rows = lay.grouped_ffn(L.FFN_ROUTED, offsets, ss)
+    shared = lay.grouped_ffn(L.FFN_SHARED)
+    torch.cuda.synchronize()
+    want, _ = _expected_rows(cfg, inp, idx, O.routing_tables(idx, cfg.E))
+    got = U.np_of(rows)[: want.shape[0]]
+    lit, beyond = U.output_errors(got, want, "f32")
+    U.record(test="grouped_ffn_large_tiles", T=T, skew=skew, err_rows_literal=lit)
+    assert lit <= U.TOL["bf16"], f"routed rows error {lit}"
+    X = np.asarray(O.x_f32(inp), np.float32)
+    want_s = O.shared_ffn(inp, cfg, X)
+    lit_s, _ = U.output_errors(U.np_of(shared), want_s, "f32")
+    U.record(test="grouped_ffn_large_tiles_shared", T=T, err_rows_literal=lit_s)
+    assert lit_s <= U.TOL["bf16"], f"shared rows error {lit_s}"
 
 
 # ----------------------------------------------------------------------------
