@@ -57,11 +57,16 @@ def parse():
     return p.parse_args()
 
 
+# Sources that define the gate/up launch the traffic counters describe: its
+# kernel, the headers it includes, and the host code that sizes its launch.
+TRAFFIC_SOURCES = ("gemm_lds.hip", "tiles.h", "common.h", "kernels.h", "api.cpp")
+
+
 def kernel_hash() -> str:
-    """Hash of every kernel and host source of libmoe.so: counters taken on
-    one version do not describe another."""
+    """Hash of the sources of the counted kernel and its launch: counters
+    taken on one version do not describe another."""
     h = hashlib.sha256()
-    for name in sorted(os.listdir(CSRC)):
+    for name in TRAFFIC_SOURCES:
         with open(os.path.join(CSRC, name), "rb") as f:
             h.update(name.encode() + f.read())
     return h.hexdigest()[:16]

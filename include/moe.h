@@ -233,7 +233,7 @@ moe_status moe_route_topk(const moe_desc* desc, const moe_weights* w,
  * (inverse: sorted_slot[slot_pos[s]] == s). An id outside [0, E) is dropped:
  * it is not counted and its slot_pos is -1. Bit-exact and deterministic.
  * Workspace: moe_workspace_bytes(desc, MOE_OP_PERMUTE), 0 up to 8192 slots
- * (one workgroup), else a per-chunk histogram of ceil(T*k/8192) * E int32.
+ * (one workgroup), else a per-chunk histogram of ceil(T*k/2048) * E int32.
  */
 moe_status moe_permute(const moe_desc* desc, const int32_t* topk_idx,
                        int32_t* counts, int32_t* offsets, int32_t* sorted_slot,

@@ -128,10 +128,11 @@ hipError_t launch_router_small(const RouterArgs& a, bool f32, hipStream_t stream
 // ---------------------------------------------------------------------------
 // Stable counting sort of slots by expert (permute.hip)
 // ---------------------------------------------------------------------------
-// Slots per workgroup of the multi-workgroup permutation (more slots than
-// this use permute_chunks(n) workgroups and a chunk_hist workspace of
-// permute_chunks(n) * E ints; fewer use one workgroup and no workspace).
-constexpr int PERMUTE_CHUNK = 8192;
+// Up to PERMUTE_ONE_WG slots the permutation runs on one workgroup with no
+// workspace; more use permute_chunks(n) workgroups of PERMUTE_CHUNK slots
+// and a chunk_hist workspace of permute_chunks(n) * E ints.
+constexpr int PERMUTE_ONE_WG = 8192;
+constexpr int PERMUTE_CHUNK = 2048;
 int permute_chunks(int n_slots);
 hipError_t launch_permute(const int* topk_idx, int n_slots, int E, int* counts, int* offsets,
                           int* sorted_slot, int* slot_pos, int* chunk_hist, hipStream_t stream);

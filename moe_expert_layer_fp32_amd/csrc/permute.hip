@@ -18,8 +18,8 @@
 //     order (stable), which fixes the permutation uniquely.
 // Ids outside [0, E) are not counted; their slot_pos is -1.
 //
-// Many slots (prefill: T*k = 65536) spread the same steps over several
-// workgroups, each owning a contiguous chunk of slots: one pass histograms
+// Many slots (more than 8192; prefill: T*k = 65536) spread the same steps
+// over several workgroups, each owning a contiguous chunk of 2048 slots: one pass histograms
 // every chunk into the workspace; a second pass gives each chunk its
 // starting position per expert (the expert's offset plus the counts of the
 // chunks before it, summed in chunk order) and places the chunk's slots as
@@ -158,7 +158,7 @@ __global__ __launch_bounds__(PERM_THREADS) void permute_kernel(const int* __rest
   }
 }
 
-int permute_chunks(int n_slots) { return n_slots > PERMUTE_CHUNK ? ceil_div(n_slots, PERMUTE_CHUNK) : 1; }
+int permute_chunks(int n_slots) { return n_slots > PERMUTE_ONE_WG ? ceil_div(n_slots, PERMUTE_CHUNK) : 1; }
 
 hipError_t launch_permute(const int* topk_idx, int n_slots, int E, int* counts, int* offsets,
                           int* sorted_slot, int* slot_pos, int* chunk_hist, hipStream_t stream) {

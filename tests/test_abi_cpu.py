@@ -57,7 +57,7 @@ def test_workspace_and_packed_sizes(L, name):
     d = L.desc_from_config(cfg)
     assert L.moe_workspace_bytes(d, L.OP_LAYER) > 0
     slots = cfg.T * cfg.k
-    assert L.moe_workspace_bytes(d, L.OP_PERMUTE) == (0 if slots <= 8192 else -(-slots // 8192) * cfg.E * 4)
+    assert L.moe_workspace_bytes(d, L.OP_PERMUTE) == (0 if slots <= 8192 else -(-slots // 2048) * cfg.E * 4)
     wb = {"f32": 4, "bf16": 2, "w8a8": 1}[cfg.dtype]
     assert L.moe_packed_bytes(d, L.PACK_W13) == cfg.n_ffn * cfg.d * cfg.inter * 2 * wb
     assert L.moe_packed_bytes(d, L.PACK_W2) == cfg.n_ffn * cfg.d * cfg.inter * wb
