@@ -315,9 +315,12 @@ moe_status run_routed(GemmArgs g, const moe_desc* d, GemmElem el, int planes, Ge
       return MOE_OK;
     }
     HIP_TRY(launch_gemm_lds(g, L, el, planes, epi, s, KernelEvents{ev.start, nullptr}));
+    // experts with more rows: 128-row tiles, 64 features per wavefront for
+    // one-plane products (twice the matrix-core work per weight fragment)
     L.tile_rows = 128;
     L.min_rows = 65;
     L.max_rows = INT32_MAX;
+    L.wave_features = planes == 1 && g.N % 256 == 0 ? 64 : 32;
     g.tiles_y = ceil_div(r_max(d), L.tile_rows) + g.n_groups;
     HIP_TRY(launch_gemm_lds(g, L, el, planes, epi, s, KernelEvents{nullptr, ev.stop}));
     return MOE_OK;

@@ -407,20 +407,18 @@ static hipError_t launch_lds_one(const GemmArgs& a, const LdsArgs& L, hipStream_
                             stream, ev.stop);
 }
 
-// Products with two or three weight planes always use 32 features per
-// wavefront: the 64-feature, 128-row tile would need more than the 512
-// registers of a lane.
+// 64 features per wavefront for one-plane products only: with two or three
+// planes the 64-feature, 128-row tile needs more than the 512 registers of a
+// lane (measured: 287 spilled registers with a 4-step ring).
 template <class Tr, int S, int EPI>
 static hipError_t launch_lds_shape(const GemmArgs& a, const LdsArgs& L, hipStream_t stream, KernelEvents ev) {
-  if (S >= 2 || L.wave_features == 32) {
-    return L.tile_rows == 64 ? launch_lds_one<Tr, S, EPI, 32, 64>(a, L, stream, ev)
-                             : launch_lds_one<Tr, S, EPI, 32, 128>(a, L, stream, ev);
-  }
   if constexpr (S == 1) {
-    return L.tile_rows == 64 ? launch_lds_one<Tr, S, EPI, 64, 64>(a, L, stream, ev)
-                             : launch_lds_one<Tr, S, EPI, 64, 128>(a, L, stream, ev);
+    if (L.wave_features == 64)
+      return L.tile_rows == 64 ? launch_lds_one<Tr, S, EPI, 64, 64>(a, L, stream, ev)
+                               : launch_lds_one<Tr, S, EPI, 64, 128>(a, L, stream, ev);
   }
-  return hipErrorInvalidValue;
+  return L.tile_rows == 64 ? launch_lds_one<Tr, S, EPI, 32, 64>(a, L, stream, ev)
+                           : launch_lds_one<Tr, S, EPI, 32, 128>(a, L, stream, ev);
 }
 
 hipError_t launch_gemm_lds(const GemmArgs& a, const LdsArgs& L, GemmElem elem, int planes, GemmEpi epi,

@@ -102,68 +102,17 @@ __device__ inline void merge_top2_dpp(float& t1, float& t2) {
 // the FW sums meet in LDS and are added in wavefront order; every wavefront
 // then runs the same gate on the same tokens (no wavefront leaves before the
 // last barrier) and only the first writes the result.
-template <int PL, int FW>
-__global__ __launch_bounds__(FW * WAVE) void gate_topk_kernel(GateArgs a) {
-  __shared__ float sc_lds[GATE_TOKENS][PL * ROW];
-  __shared__ float fold[FW][GATE_TOKENS][PL * ROW];
-  const int lane = threadIdx.x & (WAVE - 1);
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / WAVE);
-  const int r = lane & (ROW - 1), row = lane / ROW;
-  const int t_raw = blockIdx.x * GATE_TOKENS + row;
-  const bool live = t_raw < a.T;            // dead rows work on a valid token and write nothing
-  const int t = live ? t_raw : a.T - 1;
-
-  float u[PL], sc[PL];
+// Gate and selection for one token held by a row of 16 lanes (lane r holds
+// experts i*16 + r). u: its logits, bias included. sc_row: the row's LDS
+// scratch for its scores (written and read by this wavefront only). Lane
+// r < k gets selection r: sel_out (expert id) and w_out (its weight). Every
+// lane of the wavefront must be active.
+template <int PL>
+__device__ __forceinline__ void gate_row(const GateArgs& a, float (&u)[PL], const bool (&valid)[PL], int r,
+                                         float* sc_row, int& sel_out, float& w_out) {
+  float sc[PL];
   uint32_t ob[PL];
-  bool valid[PL];
   int grp[PL];
-#pragma unroll
-  for (int i = 0; i < PL; ++i) {
-    const int e = i * ROW + r;
-    valid[i] = e < a.E;
-    u[i] = 0.f;
-  }
-  if (!a.partial) {
-#pragma unroll
-    for (int i = 0; i < PL; ++i)
-      if (valid[i]) u[i] = a.z[size_t(t) * a.ldz + i * ROW + r];
-  } else {
-    // This wavefront's splits, GATE_SPLIT_BATCH loads at a time (clamped
-    // split index: every address is valid; absent splits add +0).
-    float mine[PL];
-#pragma unroll
-    for (int i = 0; i < PL; ++i) mine[i] = 0.f;
-    for (int sp0 = wave; sp0 < a.splits; sp0 += GATE_SPLIT_BATCH * FW) {
-      float part[GATE_SPLIT_BATCH][PL];
-#pragma unroll
-      for (int q = 0; q < GATE_SPLIT_BATCH; ++q) {
-        const float* P = a.partial + (size_t(min(sp0 + q * FW, a.splits - 1)) * a.T + t) * a.ldz + r;
-#pragma unroll
-        for (int i = 0; i < PL; ++i) part[q][i] = P[min(i * ROW, a.ldz - ROW)];
-      }
-#pragma unroll
-      for (int q = 0; q < GATE_SPLIT_BATCH; ++q)
-#pragma unroll
-        for (int i = 0; i < PL; ++i) mine[i] += (sp0 + q * FW < a.splits && valid[i]) ? part[q][i] : 0.f;
-    }
-    if (FW == 1) {
-#pragma unroll
-      for (int i = 0; i < PL; ++i) u[i] = mine[i];
-    } else {
-#pragma unroll
-      for (int i = 0; i < PL; ++i) fold[wave][row][i * ROW + r] = mine[i];
-      __syncthreads();
-#pragma unroll
-      for (int w = 0; w < FW; ++w)
-#pragma unroll
-        for (int i = 0; i < PL; ++i) u[i] += fold[w][row][i * ROW + r];
-    }
-    if (a.bias) {
-#pragma unroll
-      for (int i = 0; i < PL; ++i)
-        if (valid[i]) u[i] += a.bias[i * ROW + r];
-    }
-  }
 #pragma unroll
   for (int i = 0; i < PL; ++i) {
     if (!valid[i]) u[i] = -INFINITY;
@@ -189,7 +138,7 @@ __global__ __launch_bounds__(FW * WAVE) void gate_topk_kernel(GateArgs a) {
     for (int i = 0; i < PL; ++i) sc[i] = valid[i] ? 1.0f / (1.0f + expf(-u[i])) : 0.f;
   }
 #pragma unroll
-  for (int i = 0; i < PL; ++i) sc_lds[row][i * ROW + r] = sc[i];
+  for (int i = 0; i < PL; ++i) sc_row[i * ROW + r] = sc[i];
 
   bool cand[PL];
 #pragma unroll
@@ -264,13 +213,79 @@ __global__ __launch_bounds__(FW * WAVE) void gate_topk_kernel(GateArgs a) {
     drop(cand, win, r);
     if (r == j) sel_e = win;
   }
-  __syncthreads();   // scores of the row are in LDS
+  __threadfence_block();   // the row's scores are in LDS (written by this wavefront)
   const bool mine = r < a.k && sel_e >= 0;
-  const float s = mine ? sc_lds[row][sel_e] : 0.f;
+  const float s = mine ? sc_row[sel_e] : 0.f;
   const float total = row_sum_f32(s);
+  sel_out = sel_e;
+  w_out = (a.renorm ? s / total : s) * a.route_scale;
+}
+
+
+template <int PL, int FW>
+__global__ __launch_bounds__(FW * WAVE) void gate_topk_kernel(GateArgs a) {
+  __shared__ float sc_lds[GATE_TOKENS][PL * ROW];
+  __shared__ float fold[FW][GATE_TOKENS][PL * ROW];
+  const int lane = threadIdx.x & (WAVE - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / WAVE);
+  const int r = lane & (ROW - 1), row = lane / ROW;
+  const int t_raw = blockIdx.x * GATE_TOKENS + row;
+  const bool live = t_raw < a.T;            // dead rows work on a valid token and write nothing
+  const int t = live ? t_raw : a.T - 1;
+
+  float u[PL];
+  bool valid[PL];
+#pragma unroll
+  for (int i = 0; i < PL; ++i) {
+    const int e = i * ROW + r;
+    valid[i] = e < a.E;
+    u[i] = 0.f;
+  }
+  if (!a.partial) {
+#pragma unroll
+    for (int i = 0; i < PL; ++i)
+      if (valid[i]) u[i] = a.z[size_t(t) * a.ldz + i * ROW + r];
+  } else {
+    // This wavefront's splits, GATE_SPLIT_BATCH loads at a time (clamped
+    // split index: every address is valid; absent splits add +0).
+    float mine[PL];
+#pragma unroll
+    for (int i = 0; i < PL; ++i) mine[i] = 0.f;
+    for (int sp0 = wave; sp0 < a.splits; sp0 += GATE_SPLIT_BATCH * FW) {
+      float part[GATE_SPLIT_BATCH][PL];
+#pragma unroll
+      for (int q = 0; q < GATE_SPLIT_BATCH; ++q) {
+        const float* P = a.partial + (size_t(min(sp0 + q * FW, a.splits - 1)) * a.T + t) * a.ldz + r;
+#pragma unroll
+        for (int i = 0; i < PL; ++i) part[q][i] = P[min(i * ROW, a.ldz - ROW)];
+      }
+#pragma unroll
+      for (int q = 0; q < GATE_SPLIT_BATCH; ++q)
+#pragma unroll
+        for (int i = 0; i < PL; ++i) mine[i] += (sp0 + q * FW < a.splits && valid[i]) ? part[q][i] : 0.f;
+    }
+    if (FW == 1) {
+#pragma unroll
+      for (int i = 0; i < PL; ++i) u[i] = mine[i];
+    } else {
+#pragma unroll
+      for (int i = 0; i < PL; ++i) fold[wave][row][i * ROW + r] = mine[i];
+      __syncthreads();
+#pragma unroll
+      for (int w = 0; w < FW; ++w)
+#pragma unroll
+        for (int i = 0; i < PL; ++i) u[i] += fold[w][row][i * ROW + r];
+    }
+    if (a.bias) {
+#pragma unroll
+      for (int i = 0; i < PL; ++i)
+        if (valid[i]) u[i] += a.bias[i * ROW + r];
+    }
+  }
+  int sel_e;
+  float wv;
+  gate_row<PL>(a, u, valid, r, &sc_lds[row][0], sel_e, wv);
   if (wave == 0 && live && r < a.k) {
-    float wv = a.renorm ? s / total : s;
-    wv *= a.route_scale;
     a.topk_idx[size_t(t) * a.k + r] = sel_e;
     a.topk_w[size_t(t) * a.k + r] = wv;
   }
