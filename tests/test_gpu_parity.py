@@ -484,6 +484,35 @@ def test_layer_single_token():
         assert beyond <= U.TOL[cfg.dtype]
 
 
+@pytest.mark.parametrize("dtype,gate", [("f32", "softmax"), ("bf16", "sigmoid"), ("w8a8", "softmax")])
+def test_layer_odd_shapes(dtype, gate):
+    """Shapes off the tile grid (d 192, I 320, I_s 192: no 128-element
+    chunk, untiled column counts), 97 tokens, k 5 of 40 experts with
+    resident FFN ids 3..22, identity ids 30..35 and the rest held elsewhere."""
+    L, DeviceLayer, to_device = _L()
+    cfg = MoEConfig(name="odd", T=97, d=192, E=40, k=5, gate=gate, ffn_begin=3, n_ffn=20, zero_begin=30, n_zero=6,
+                    inter=320, shared_inter=192, dtype=dtype, route_scale=1.25)
+    inp = make_inputs(cfg)
+    U.say(f"[gpu] layer odd shapes {dtype} {gate}")
+    _check_layer(cfg, inp, DeviceLayer(cfg, inp))
+
+
+def test_layer_largest_k_group_limited():
+    """k = 16 (the largest built), group-limited selection of 4 of 8 groups
+    over 256 experts, 16 resident, two streams."""
+    L, DeviceLayer, to_device = _L()
+    from moe_expert_layer_fp32_amd.layer import SecondStream
+    cfg = MoEConfig(name="k16", T=64, d=256, E=256, k=16, gate="sigmoid", n_group=8, topk_group=4, n_ffn=16,
+                    inter=128, shared_inter=128, dtype="bf16")
+    inp = make_inputs(cfg)
+    U.say("[gpu] layer k=16 group-limited")
+    lay = DeviceLayer(cfg, inp)
+    y = _check_layer(cfg, inp, lay)
+    two = lay.layer(second=SecondStream())
+    torch.cuda.synchronize()
+    assert torch.equal(_bits(y), _bits(two))
+
+
 def test_layer_all_identity_experts():
     """Every expert a zero-computation expert: y = route_scale * x, rounded once."""
     L, DeviceLayer, to_device = _L()
