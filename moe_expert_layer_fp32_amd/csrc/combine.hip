@@ -8,8 +8,9 @@
 // zero-computation expert contributes its input (page "LongCat-Flash与
 // GLM-4.6V ...", section 拆解MoE困局), read straight from x: it never enters
 // the expert rows. One workgroup per token; each thread owns 4 consecutive
-// columns; the sum runs in fp32 in a fixed order (shared, then slot 0..k-1)
-// and is rounded once, so the result is deterministic without atomics.
+// columns; the sum runs in fp32 in a fixed order (shared row, the expert
+// rows in slot order, then x times the summed identity weights) and is
+// rounded once, so the result is deterministic without atomics.
 #include "common.h"
 #include "kernels.h"
 
@@ -18,50 +19,64 @@ namespace moe {
 constexpr int COMB_THREADS = 256;
 constexpr int COMB_MAX_K = 16;
 
+// KMAX >= k: the rows of a column chunk are all loaded before any is added,
+// so the loads of a chunk are in flight together. Sum order: shared row,
+// expert rows in selection order, then the identity part (x times the
+// summed identity weights).
+template <int KMAX>
 __global__ __launch_bounds__(COMB_THREADS) void combine_kernel(CombineArgs a) {
   const int t = blockIdx.x;
-  __shared__ int s_kind[COMB_MAX_K];    // 0 absent, 1 ffn row, 2 identity
+  // The token's expert rows in selection order (compacted), their weights,
+  // and the summed weight of its identity selections.
   __shared__ int s_row[COMB_MAX_K];
   __shared__ float s_w[COMB_MAX_K];
-  if (threadIdx.x < a.k) {
-    const int j = threadIdx.x;
-    const int e = a.topk_idx[size_t(t) * a.k + j];
-    int kind = 0, row = -1;
-    if (e >= a.ffn_begin && e < a.ffn_begin + a.n_ffn) {
-      const int p = a.slot_pos[size_t(t) * a.k + j];
-      if (p >= 0) {
-        kind = 1;
-        row = p - a.offsets[a.ffn_begin];
+  __shared__ int s_n;
+  __shared__ float s_wid;
+  if (threadIdx.x == 0) {
+    int n = 0;
+    float wid = 0.f;
+    for (int j = 0; j < a.k; ++j) {
+      const int e = a.topk_idx[size_t(t) * a.k + j];
+      const float w = a.topk_w[size_t(t) * a.k + j];
+      if (e >= a.ffn_begin && e < a.ffn_begin + a.n_ffn) {
+        const int p = a.slot_pos[size_t(t) * a.k + j];
+        if (p >= 0) {
+          s_row[n] = p - a.offsets[a.ffn_begin];
+          s_w[n] = w;
+          ++n;
+        }
+      } else if (e >= a.zero_begin && e < a.zero_begin + a.n_zero) {
+        wid += w;
       }
-    } else if (e >= a.zero_begin && e < a.zero_begin + a.n_zero) {
-      kind = 2;
     }
-    s_kind[j] = kind;
-    s_row[j] = row;
-    s_w[j] = a.topk_w[size_t(t) * a.k + j];
+    s_n = n;
+    s_wid = wid;
   }
   __syncthreads();
+  const int n = s_n;
+  const float wid = s_wid;
   for (int c = threadIdx.x * 4; c < a.d; c += COMB_THREADS * 4) {
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     if (a.shared_rows) acc = *reinterpret_cast<const f32x4*>(a.shared_rows + size_t(t) * a.d + c);
-    for (int j = 0; j < a.k; ++j) {
-      const int kind = s_kind[j];
-      const float w = s_w[j];
-      if (kind == 1) {
-        const f32x4 u = *reinterpret_cast<const f32x4*>(a.rows + size_t(s_row[j]) * a.d + c);
-        acc += w * u;
-      } else if (kind == 2) {
-        f32x4 u;
-        if (a.x_bf16) {
-          const u32x2 p = *reinterpret_cast<const u32x2*>(static_cast<const uint16_t*>(a.x) + size_t(t) * a.d + c);
-          u = f32x4{__uint_as_float(p[0] << 16), __uint_as_float(p[0] & 0xFFFF0000u),
-                    __uint_as_float(p[1] << 16), __uint_as_float(p[1] & 0xFFFF0000u)};
-        } else {
-          u = *reinterpret_cast<const f32x4*>(static_cast<const float*>(a.x) + size_t(t) * a.d + c);
-        }
-        acc += w * u;
+    // all row loads of the chunk first (n is the same for the workgroup)
+    f32x4 u[KMAX];
+#pragma unroll
+    for (int q = 0; q < KMAX; ++q)
+      if (q < n) u[q] = *reinterpret_cast<const f32x4*>(a.rows + size_t(s_row[q]) * a.d + c);
+    f32x4 ux = {0.f, 0.f, 0.f, 0.f};
+    if (wid != 0.f) {
+      if (a.x_bf16) {
+        const u32x2 p = *reinterpret_cast<const u32x2*>(static_cast<const uint16_t*>(a.x) + size_t(t) * a.d + c);
+        ux = f32x4{__uint_as_float(p[0] << 16), __uint_as_float(p[0] & 0xFFFF0000u), __uint_as_float(p[1] << 16),
+                   __uint_as_float(p[1] & 0xFFFF0000u)};
+      } else {
+        ux = *reinterpret_cast<const f32x4*>(static_cast<const float*>(a.x) + size_t(t) * a.d + c);
       }
     }
+#pragma unroll
+    for (int q = 0; q < KMAX; ++q)
+      if (q < n) acc += s_w[q] * u[q];
+    if (wid != 0.f) acc += wid * ux;
     if (a.x_bf16) {
       u32x2 p;
       p[0] = uint32_t(f32_to_bf16(acc[0])) | (uint32_t(f32_to_bf16(acc[1])) << 16);
@@ -75,7 +90,11 @@ __global__ __launch_bounds__(COMB_THREADS) void combine_kernel(CombineArgs a) {
 
 hipError_t launch_combine(const CombineArgs& a, hipStream_t stream) {
   if (a.T <= 0) return hipSuccess;
-  hipLaunchKernelGGL(combine_kernel, dim3(a.T), dim3(COMB_THREADS), 0, stream, a);
+  const dim3 grid(a.T), block(COMB_THREADS);
+  if (a.k <= 2) hipLaunchKernelGGL(combine_kernel<2>, grid, block, 0, stream, a);
+  else if (a.k <= 4) hipLaunchKernelGGL(combine_kernel<4>, grid, block, 0, stream, a);
+  else if (a.k <= 8) hipLaunchKernelGGL(combine_kernel<8>, grid, block, 0, stream, a);
+  else hipLaunchKernelGGL(combine_kernel<16>, grid, block, 0, stream, a);
   return hipGetLastError();
 }
 
