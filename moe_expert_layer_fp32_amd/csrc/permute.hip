@@ -32,6 +32,8 @@ namespace moe {
 constexpr int PERM_WAVES = 16;
 constexpr int PERM_THREADS = PERM_WAVES * WAVE;
 constexpr int PERM_MAX_E = 256;
+constexpr int PERM_SEG_IDS = PERMUTE_ONE_WG / PERM_THREADS;   // ids per lane of a segment
+static_assert(PERMUTE_CHUNK <= PERMUTE_ONE_WG, "a chunk must fit one workgroup's registers");
 
 // Histogram of the chunk [chunk * blockIdx.x, ...) of each workgroup into
 // chunk_hist[blockIdx.x][E] (integer LDS atomics: order-independent).
@@ -72,8 +74,18 @@ __global__ __launch_bounds__(PERM_THREADS) void permute_kernel(const int* __rest
   const int seg0 = min(c1, c0 + wave * seg_len);
   const int seg1 = min(c1, seg0 + seg_len);
 
-  for (int s = seg0 + lane; s < seg1; s += WAVE) {
-    const int e = idx[s];
+  // The segment's ids stay in registers for the placement below (segments
+  // are at most PERM_SEG_IDS * 64 slots: one workgroup takes at most
+  // PERMUTE_ONE_WG slots, a chunk PERMUTE_CHUNK).
+  int ids[PERM_SEG_IDS];
+#pragma unroll
+  for (int q = 0; q < PERM_SEG_IDS; ++q) {
+    const int s = seg0 + q * WAVE + lane;
+    ids[q] = s < seg1 ? idx[s] : -1;
+  }
+#pragma unroll
+  for (int q = 0; q < PERM_SEG_IDS; ++q) {
+    const int e = ids[q];
     if (e >= 0 && e < E) atomicAdd(&hist[wave][e], 1);
   }
   __syncthreads();
@@ -131,10 +143,13 @@ __global__ __launch_bounds__(PERM_THREADS) void permute_kernel(const int* __rest
   int nbits = 0;
   while ((1 << nbits) < E) ++nbits;
   const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (WAVE - lane));
-  for (int c = seg0; c < seg1; c += WAVE) {
+#pragma unroll
+  for (int q = 0; q < PERM_SEG_IDS; ++q) {
+    const int c = seg0 + q * WAVE;
+    if (c >= seg1) break;   // wavefront-uniform
     const int s = c + lane;
     const bool in = s < seg1;
-    const int e = in ? idx[s] : -1;
+    const int e = in ? ids[q] : -1;
     const bool ok = in && e >= 0 && e < E;
     uint64_t same = __ballot(ok);
     for (int b = 0; b < nbits; ++b) {
