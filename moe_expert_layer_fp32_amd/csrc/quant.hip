@@ -6,7 +6,7 @@
 // SuperPoD的LongCat-Flash模型推理性能优化实践", section 优化措施三). Rule,
 // per row: s = amax / 127 and q = clamp(rint(v / s), -127, 127), in fp32
 // with correctly rounded division and round-half-to-even; a zero row gets
-// s = 0 and q = 0. One wavefront per row: a max reduction, then the codes.
+// s = 0 and q = 0. One workgroup per row: a max reduction, then the codes.
 #include "common.h"
 #include "kernels.h"
 
@@ -25,44 +25,73 @@ __device__ inline void load4(const void* in, int in_bf16, size_t off, float v[4]
   }
 }
 
-__global__ __launch_bounds__(256) void quant_rows_kernel(const void* in, int in_bf16, int cols, int max_rows,
-                                                         const int* offsets, int first, int n_groups,
-                                                         int8_t* q, float* s) {
-  const int lane = threadIdx.x & (WAVE - 1);
-  const int r = blockIdx.x * (blockDim.x / WAVE) + threadIdx.x / WAVE;
+// One workgroup of QUANT_THREADS per row: each thread loads its QUANT_V
+// 4-column groups of the row in one batch (strided by the workgroup, so
+// every load instruction is contiguous across the workgroup) and keeps them
+// in registers, the row maximum meets in LDS, and the codes are made from
+// the registers. Rows longer than QUANT_THREADS * QUANT_V * 4 take several
+// batches (the second pass re-reads them).
+constexpr int QUANT_THREADS = 256;
+constexpr int QUANT_V = 8;
+
+__global__ __launch_bounds__(QUANT_THREADS) void quant_rows_kernel(const void* in, int in_bf16, int cols,
+                                                                   int max_rows, const int* offsets, int first,
+                                                                   int n_groups, int8_t* q, float* s) {
+  __shared__ float wmax[QUANT_THREADS / WAVE];
+  const int r = blockIdx.x;
   const int rows = offsets ? offsets[first + n_groups] - offsets[first] : max_rows;
-  if (r >= rows) return;
+  if (r >= rows) return;   // whole workgroup
+  const int lane = threadIdx.x & (WAVE - 1), wave = threadIdx.x / WAVE;
   const size_t base = size_t(r) * cols;
-  float amax = 0.f;
-  for (int c = lane * 4; c < cols; c += WAVE * 4) {
-    float v[4];
-    load4(in, in_bf16, base + c, v);
+  constexpr int STEP = QUANT_THREADS * 4;   // columns per batch entry
+  const int batches = ceil_div(cols, STEP * QUANT_V);
+  float v[QUANT_V][4];
+  auto load_batch = [&](int b) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) amax = fmaxf(amax, fabsf(v[j]));
+    for (int i = 0; i < QUANT_V; ++i) {
+      const int c = (b * QUANT_V + i) * STEP + threadIdx.x * 4;
+      if (c < cols) load4(in, in_bf16, base + c, v[i]);
+      else v[i][0] = v[i][1] = v[i][2] = v[i][3] = 0.f;
+    }
+  };
+  float amax = 0.f;
+  for (int b = 0; b < batches; ++b) {
+    load_batch(b);
+#pragma unroll
+    for (int i = 0; i < QUANT_V; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) amax = fmaxf(amax, fabsf(v[i][j]));
   }
   amax = wave_max(amax);
-  const float sc = amax / 127.0f;
-  for (int c = lane * 4; c < cols; c += WAVE * 4) {
-    float v[4];
-    load4(in, in_bf16, base + c, v);
-    uint32_t packed = 0;
+  if (lane == 0) wmax[wave] = amax;
+  __syncthreads();
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      float qf = 0.f;
-      if (sc > 0.f) qf = fminf(fmaxf(rintf(v[j] / sc), -127.f), 127.f);
-      packed |= (uint32_t(int32_t(qf)) & 0xFFu) << (8 * j);
+  for (int w = 0; w < QUANT_THREADS / WAVE; ++w) amax = fmaxf(amax, wmax[w]);
+  const float sc = amax / 127.0f;
+  for (int b = 0; b < batches; ++b) {
+    if (batches > 1) load_batch(b);   // one batch: the registers still hold the row
+#pragma unroll
+    for (int i = 0; i < QUANT_V; ++i) {
+      const int c = (b * QUANT_V + i) * STEP + threadIdx.x * 4;
+      if (c >= cols) continue;
+      uint32_t packed = 0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        float qf = 0.f;
+        if (sc > 0.f) qf = fminf(fmaxf(rintf(v[i][j] / sc), -127.f), 127.f);
+        packed |= (uint32_t(int32_t(qf)) & 0xFFu) << (8 * j);
+      }
+      *reinterpret_cast<uint32_t*>(q + base + c) = packed;
     }
-    *reinterpret_cast<uint32_t*>(q + base + c) = packed;
   }
-  if (lane == 0) s[r] = sc;
+  if (threadIdx.x == 0) s[r] = sc;
 }
 
 hipError_t launch_quant_rows(const void* in, int in_bf16, int cols, int max_rows, const int* offsets,
                              int first, int n_groups, int8_t* q, float* s, hipStream_t stream) {
   if (max_rows <= 0) return hipSuccess;
-  constexpr int waves = 4;
-  hipLaunchKernelGGL(quant_rows_kernel, dim3(ceil_div(max_rows, waves)), dim3(waves * WAVE), 0, stream,
-                     in, in_bf16, cols, max_rows, offsets, first, n_groups, q, s);
+  hipLaunchKernelGGL(quant_rows_kernel, dim3(max_rows), dim3(QUANT_THREADS), 0, stream, in, in_bf16, cols, max_rows,
+                     offsets, first, n_groups, q, s);
   return hipGetLastError();
 }
 
