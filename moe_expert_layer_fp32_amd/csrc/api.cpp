@@ -48,6 +48,11 @@ int weight_kf(const moe_desc* d) { return d->dtype == MOE_DTYPE_F32 ? 4 : (d->dt
 int frag_bytes_of(GemmElem e) { return e == ELEM_F32 ? 64 * 4 : 64 * 16; }
 int kf_of(GemmElem e) { return e == ELEM_F32 ? 4 : (e == ELEM_BF16 ? 32 : 64); }
 GemmElem router_elem(const moe_desc* d) { return d->dtype == MOE_DTYPE_F32 ? ELEM_F32 : ELEM_BF16; }
+// Bytes per element of the expert outputs moe_layer keeps in its workspace:
+// bf16 layers keep them in bf16 (the sum over experts still runs in fp32),
+// fp32 and W8A8 layers in fp32 (W8A8 rows already carry the int8 error of
+// x and h; a further bf16 rounding would add to it).
+size_t layer_row_bytes(const moe_desc* d) { return d->dtype == MOE_DTYPE_BF16 ? 2 : 4; }
 
 // ---------------------------------------------------------------------------
 // Which kernel runs each product (decided on the host from shapes only; the
@@ -222,7 +227,7 @@ struct LayerWs {
   int32_t* chunk_hist;
   float* w;
   FfnWs routed, shared;
-  float *rows, *shared_rows;
+  void *rows, *shared_rows;   // expert outputs: bf16 for bf16 / W8A8 layers, else fp32
 };
 LayerWs carve_layer(Carve& c, const moe_desc* d) {
   LayerWs L{};
@@ -240,11 +245,11 @@ LayerWs carve_layer(Carve& c, const moe_desc* d) {
   L.shared.sx = L.routed.sx;
   carve_h(c, d, r_max(d), d->inter, L.routed);
   L.routed.partial = c.take(routed_partial_bytes(d));
-  L.rows = static_cast<float*>(c.take(size_t(r_max(d)) * d->d * 4));
+  L.rows = c.take(size_t(r_max(d)) * d->d * layer_row_bytes(d));
   if (d->shared_inter > 0) {
     carve_h(c, d, d->T, d->shared_inter, L.shared);
     L.shared.partial = c.take(dense_partial_bytes(d, false, true));
-    L.shared_rows = static_cast<float*>(c.take(size_t(d->T) * d->d * 4));
+    L.shared_rows = c.take(size_t(d->T) * d->d * layer_row_bytes(d));
   } else {
     L.shared_rows = nullptr;
   }
@@ -410,7 +415,7 @@ struct FfnPlan {
   int rows_bound;              // routed: r_max; shared: T
 };
 
-moe_status run_ffn(const moe_desc* d, const FfnPlan& p, const void* x, const FfnWs& f, float* rows,
+moe_status run_ffn(const moe_desc* d, const FfnPlan& p, const void* x, const FfnWs& f, void* rows, bool rows_bf16,
                    hipStream_t s, hipEvent_t e1b, hipEvent_t e1e, hipEvent_t e2b, hipEvent_t e2e) {
   const GemmElem el = weight_elem(d);
   const int FB = frag_bytes_of(el);
@@ -462,9 +467,9 @@ moe_status run_ffn(const moe_desc* d, const FfnPlan& p, const void* x, const Ffn
   g2.n_groups = p.groups;
   g2.dense_rows = d->T;
   g2.sorted_slot = nullptr;
-  g2.out = reinterpret_cast<uint8_t*>(rows);
-  g2.ldo = size_t(d->d) * 4;
-  g2.out_bf16 = 0;
+  g2.out = static_cast<uint8_t*>(rows);
+  g2.ldo = size_t(d->d) * (rows_bf16 ? 2 : 4);
+  g2.out_bf16 = rows_bf16;
   st = routed ? run_routed(g2, d, el, 1, EPI_SUM, f.partial, s, ev2)
               : run_dense(g2, d->T, el, 1, EPI_SUM, f.partial, s, ev2);
   if (st != MOE_OK) return st;
@@ -491,7 +496,7 @@ bool shared_weights_ok(const moe_desc* d, const moe_weights* w) {
   return true;
 }
 
-CombineArgs combine_args(const moe_desc* d, const void* x, const float* rows, const float* shared_rows,
+CombineArgs combine_args(const moe_desc* d, const void* x, const void* rows, const void* shared_rows, bool rows_bf16,
                          const int32_t* idx, const float* tw, const int32_t* offsets, const int32_t* slot_pos,
                          void* y) {
   CombineArgs c{};
@@ -499,6 +504,7 @@ CombineArgs combine_args(const moe_desc* d, const void* x, const float* rows, co
   c.x_bf16 = d->dtype != MOE_DTYPE_F32;
   c.rows = rows;
   c.shared_rows = shared_rows;
+  c.rows_bf16 = rows_bf16;
   c.topk_idx = idx;
   c.topk_w = tw;
   c.offsets = offsets;
@@ -652,7 +658,7 @@ moe_status moe_grouped_ffn(const moe_desc* d, const moe_weights* w, int which, c
     if (st != MOE_OK) return st;
   }
   const FfnPlan p = routed ? routed_plan(d, w, offsets, sorted_slot) : shared_plan(d, w);
-  return run_ffn(d, p, x, f, rows, s, nullptr, nullptr, nullptr, nullptr);
+  return run_ffn(d, p, x, f, rows, false, s, nullptr, nullptr, nullptr, nullptr);
 }
 
 moe_status moe_combine(const moe_desc* d, const void* x, const float* rows, const float* shared_rows,
@@ -664,7 +670,7 @@ moe_status moe_combine(const moe_desc* d, const void* x, const float* rows, cons
   if (!x || !topk_idx || !topk_w || !y) return MOE_ERR_INVALID_ARG;
   if (d->n_ffn > 0 && (!rows || !offsets || !slot_pos)) return MOE_ERR_INVALID_ARG;
   if (d->shared_inter > 0 && !shared_rows) return MOE_ERR_INVALID_ARG;
-  const CombineArgs c = combine_args(d, x, rows, d->shared_inter > 0 ? shared_rows : nullptr, topk_idx, topk_w,
+  const CombineArgs c = combine_args(d, x, rows, d->shared_inter > 0 ? shared_rows : nullptr, false, topk_idx, topk_w,
                                      offsets, slot_pos, y);
   return launch_combine(c, static_cast<hipStream_t>(stream)) == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
@@ -685,6 +691,7 @@ moe_status moe_layer(const moe_desc* d, const moe_weights* w, const void* x, voi
   hipStream_t s = static_cast<hipStream_t>(stream);
   Carve c(ws);
   LayerWs L = carve_layer(c, d);
+  const bool rb = layer_row_bytes(d) == 2;
   moe_aux none{};
   const moe_aux& A = aux ? *aux : none;
   int32_t* idx = A.topk_idx ? A.topk_idx : L.idx;
@@ -707,7 +714,7 @@ moe_status moe_layer(const moe_desc* d, const moe_weights* w, const void* x, voi
     hipStream_t s2 = static_cast<hipStream_t>(A.stream2);
     HIP_TRY(hipEventRecord(static_cast<hipEvent_t>(A.ev_fork), s));
     HIP_TRY(hipStreamWaitEvent(s2, static_cast<hipEvent_t>(A.ev_fork), 0));
-    st = run_ffn(d, shared_plan(d, w), x, L.shared, L.shared_rows, s2, nullptr, nullptr, nullptr, nullptr);
+    st = run_ffn(d, shared_plan(d, w), x, L.shared, L.shared_rows, rb, s2, nullptr, nullptr, nullptr, nullptr);
     if (st != MOE_OK) return st;
     HIP_TRY(hipEventRecord(static_cast<hipEvent_t>(A.ev_join), s2));
   }
@@ -718,7 +725,7 @@ moe_status moe_layer(const moe_desc* d, const moe_weights* w, const void* x, voi
   HIP_TRY(launch_permute(idx, d->T * d->k, d->E, counts, offsets, sorted_slot, slot_pos, L.chunk_hist, s));
   if (d->T == 0) return MOE_OK;
   if (d->n_ffn > 0) {
-    st = run_ffn(d, routed_plan(d, w, offsets, sorted_slot), x, L.routed, L.rows, s,
+    st = run_ffn(d, routed_plan(d, w, offsets, sorted_slot), x, L.routed, L.rows, rb, s,
                  static_cast<hipEvent_t>(A.ev_ffn1_begin), static_cast<hipEvent_t>(A.ev_ffn1_end),
                  static_cast<hipEvent_t>(A.ev_ffn2_begin), static_cast<hipEvent_t>(A.ev_ffn2_end));
     if (st != MOE_OK) return st;
@@ -726,10 +733,10 @@ moe_status moe_layer(const moe_desc* d, const moe_weights* w, const void* x, voi
   if (fork) {
     HIP_TRY(hipStreamWaitEvent(s, static_cast<hipEvent_t>(A.ev_join), 0));
   } else if (d->shared_inter > 0) {
-    st = run_ffn(d, shared_plan(d, w), x, L.shared, L.shared_rows, s, nullptr, nullptr, nullptr, nullptr);
+    st = run_ffn(d, shared_plan(d, w), x, L.shared, L.shared_rows, rb, s, nullptr, nullptr, nullptr, nullptr);
     if (st != MOE_OK) return st;
   }
-  const CombineArgs cb = combine_args(d, x, L.rows, L.shared_rows, idx, tw, offsets, slot_pos, y);
+  const CombineArgs cb = combine_args(d, x, L.rows, L.shared_rows, rb, idx, tw, offsets, slot_pos, y);
   HIP_TRY(launch_combine(cb, s));
   return MOE_OK;
 }

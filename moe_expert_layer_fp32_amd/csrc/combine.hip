@@ -13,18 +13,37 @@
 // rounded once, so the result is deterministic without atomics.
 #include "common.h"
 #include "kernels.h"
+#include <type_traits>
 
 namespace moe {
 
 constexpr int COMB_THREADS = 256;
 constexpr int COMB_MAX_K = 16;
 
+// Four consecutive values of an expert-output row, fp32 or bf16 (RB).
+template <bool RB>
+struct Row4 {
+  using raw = typename std::conditional<RB, u32x2, f32x4>::type;
+  static __device__ __forceinline__ raw load(const void* base, size_t off) {
+    return RB ? *reinterpret_cast<const raw*>(static_cast<const uint16_t*>(base) + off)
+              : *reinterpret_cast<const raw*>(static_cast<const float*>(base) + off);
+  }
+  static __device__ __forceinline__ f32x4 widen(raw v) {
+    if constexpr (RB)
+      return f32x4{__uint_as_float(v[0] << 16), __uint_as_float(v[0] & 0xFFFF0000u), __uint_as_float(v[1] << 16),
+                   __uint_as_float(v[1] & 0xFFFF0000u)};
+    else
+      return v;
+  }
+};
+
 // KMAX >= k: the rows of a column chunk are all loaded before any is added,
 // so the loads of a chunk are in flight together. Sum order: shared row,
 // expert rows in selection order, then the identity part (x times the
-// summed identity weights).
-template <int KMAX>
+// summed identity weights). RB: the expert rows are bf16.
+template <int KMAX, bool RB>
 __global__ __launch_bounds__(COMB_THREADS) void combine_kernel(CombineArgs a) {
+  using R = Row4<RB>;
   const int t = blockIdx.x;
   // The token's expert rows in selection order (compacted), their weights,
   // and the summed weight of its identity selections.
@@ -57,12 +76,12 @@ __global__ __launch_bounds__(COMB_THREADS) void combine_kernel(CombineArgs a) {
   const float wid = s_wid;
   for (int c = threadIdx.x * 4; c < a.d; c += COMB_THREADS * 4) {
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    if (a.shared_rows) acc = *reinterpret_cast<const f32x4*>(a.shared_rows + size_t(t) * a.d + c);
+    if (a.shared_rows) acc = R::widen(R::load(a.shared_rows, size_t(t) * a.d + c));
     // all row loads of the chunk first (n is the same for the workgroup)
-    f32x4 u[KMAX];
+    typename R::raw u[KMAX];
 #pragma unroll
     for (int q = 0; q < KMAX; ++q)
-      if (q < n) u[q] = *reinterpret_cast<const f32x4*>(a.rows + size_t(s_row[q]) * a.d + c);
+      if (q < n) u[q] = R::load(a.rows, size_t(s_row[q]) * a.d + c);
     f32x4 ux = {0.f, 0.f, 0.f, 0.f};
     if (wid != 0.f) {
       if (a.x_bf16) {
@@ -75,7 +94,7 @@ __global__ __launch_bounds__(COMB_THREADS) void combine_kernel(CombineArgs a) {
     }
 #pragma unroll
     for (int q = 0; q < KMAX; ++q)
-      if (q < n) acc += s_w[q] * u[q];
+      if (q < n) acc += s_w[q] * R::widen(u[q]);
     if (wid != 0.f) acc += wid * ux;
     if (a.x_bf16) {
       u32x2 p;
@@ -88,14 +107,20 @@ __global__ __launch_bounds__(COMB_THREADS) void combine_kernel(CombineArgs a) {
   }
 }
 
+template <bool RB>
+hipError_t launch_combine_k(const CombineArgs& a, hipStream_t stream) {
+  const dim3 grid(a.T), block(COMB_THREADS);
+  if (a.k <= 2) hipLaunchKernelGGL((combine_kernel<2, RB>), grid, block, 0, stream, a);
+  else if (a.k <= 4) hipLaunchKernelGGL((combine_kernel<4, RB>), grid, block, 0, stream, a);
+  else if (a.k <= 8) hipLaunchKernelGGL((combine_kernel<8, RB>), grid, block, 0, stream, a);
+  else hipLaunchKernelGGL((combine_kernel<16, RB>), grid, block, 0, stream, a);
+  return hipGetLastError();
+}
+
 hipError_t launch_combine(const CombineArgs& a, hipStream_t stream) {
   if (a.T <= 0) return hipSuccess;
-  const dim3 grid(a.T), block(COMB_THREADS);
-  if (a.k <= 2) hipLaunchKernelGGL(combine_kernel<2>, grid, block, 0, stream, a);
-  else if (a.k <= 4) hipLaunchKernelGGL(combine_kernel<4>, grid, block, 0, stream, a);
-  else if (a.k <= 8) hipLaunchKernelGGL(combine_kernel<8>, grid, block, 0, stream, a);
-  else hipLaunchKernelGGL(combine_kernel<16>, grid, block, 0, stream, a);
-  return hipGetLastError();
+  if (a.rows_bf16) return launch_combine_k<true>(a, stream);
+  return launch_combine_k<false>(a, stream);
 }
 
 }  // namespace moe

@@ -152,8 +152,9 @@ hipError_t launch_quant_rows(const void* in, int in_bf16, int cols, int max_rows
 struct CombineArgs {
   const void* x;             // [T][d] fp32 or bf16
   int x_bf16;
-  const float* rows;         // compacted routed rows [R][d]
-  const float* shared_rows;  // [T][d] or null
+  const void* rows;          // compacted routed rows [R][d]
+  const void* shared_rows;   // [T][d] or null
+  int rows_bf16;             // rows and shared_rows are bf16 (else fp32)
   const int* topk_idx;
   const float* topk_w;
   const int* offsets;        // [E+1]
