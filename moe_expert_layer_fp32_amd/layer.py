@@ -151,7 +151,7 @@ class DeviceLayer:
         L.moe_layer(self.desc_for(T), self.weights, x, y, aux, ws)
         return y
 
-    def layer_with_tables(self, x=None):
+    def layer_with_tables(self, x=None, ws=None):
         """moe_layer plus its routing tables (and W8A8 activation codes) via moe_aux."""
         x = self.x if x is None else x
         T, k, E, dev = x.shape[0], self.cfg.k, self.cfg.E, self.device
@@ -165,5 +165,5 @@ class DeviceLayer:
             t["q_x"] = torch.empty((T, self.cfg.d), dtype=torch.int8, device=dev)
             t["s_x"] = torch.empty(T, dtype=torch.float32, device=dev)
         aux = L.MoeAux(**{n: L.ptr(v) for n, v in t.items()})
-        y = self.layer(x, aux=aux)
+        y = self.layer(x, aux=aux, ws=ws)
         return y, t

@@ -381,8 +381,8 @@ LAYER_CASES = [("tiny_fp32", None), ("tiny_fp32", 333), ("longcat_zero_bf16", No
                ("dsv3_decode_share_bf16", None), ("dsv3_decode_share_bf16", 129), ("pangu_moge_w8a8", None)]
 
 
-def _check_layer(cfg, inp, lay, tokens=None):
-    y, t = lay.layer_with_tables()
+def _check_layer(cfg, inp, lay, tokens=None, ws=None):
+    y, t = lay.layer_with_tables(ws=ws)
     torch.cuda.synchronize()
     idx_gpu, w_gpu = U.np_of(t["topk_idx"]), U.np_of(t["topk_w"])
     ref = O.moe_layer(inp, cfg, tokens=tokens)
@@ -402,6 +402,7 @@ def _check_layer(cfg, inp, lay, tokens=None):
     counts, offsets, ss, sp = (U.np_of(t[n]) for n in ("counts", "offsets", "sorted_slot", "slot_pos"))
     flat = idx_gpu.reshape(-1)
     assert np.array_equal(counts, np.bincount(flat, minlength=cfg.E))
+    assert np.array_equal(offsets, np.concatenate([[0], np.cumsum(counts)]))
     assert np.array_equal(ss, np.argsort(flat, kind="stable"))
     assert np.array_equal(sp[ss], np.arange(flat.size))
     if tokens is None and not amb.any():
@@ -495,6 +496,26 @@ def test_layer_odd_shapes(dtype, gate):
     inp = make_inputs(cfg)
     U.say(f"[gpu] layer odd shapes {dtype} {gate}")
     _check_layer(cfg, inp, DeviceLayer(cfg, inp))
+
+
+@pytest.mark.parametrize("T", [1024, 1025])
+def test_layer_sort_boundary(T):
+    """T*k = 8192 slots, the most one permutation workgroup sorts, and one
+    token past it (the chunked permutation). Two calls on one workspace that
+    starts filled with 0xFF bytes give identical results."""
+    L, DeviceLayer, to_device = _L()
+    cfg = MoEConfig(name="sortb", T=T, d=256, E=64, k=8, gate="softmax", n_ffn=64, inter=128, dtype="bf16")
+    inp = make_inputs(cfg)
+    lay = DeviceLayer(cfg, inp)
+    ws = lay.workspace(L.OP_LAYER)
+    ws.fill_(255)
+    U.say(f"[gpu] layer sort boundary T={T} slots={T * cfg.k}")
+    y = _check_layer(cfg, inp, lay, ws=ws)
+    y2, t2 = lay.layer_with_tables(ws=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(_bits(y), _bits(y2))
+    flat = U.np_of(t2["topk_idx"]).reshape(-1)
+    assert np.array_equal(U.np_of(t2["sorted_slot"]), np.argsort(flat, kind="stable"))
 
 
 def test_layer_largest_k_group_limited():
