@@ -48,6 +48,8 @@ def parse():
     p.add_argument("--layers", type=int, default=0, help="layers cycled (0: enough for > 1 GB of weights)")
     p.add_argument("--cpu-seconds", type=float, default=10.0, help="target CPU time of the oracle sample")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--graph", action="store_true",
+                   help="also time the same calls replayed from one captured HIP graph (graph_replay)")
     p.add_argument("--streams", type=int, default=2, choices=(1, 2),
                    help="2: the shared expert runs on a second stream (when the workload has one)")
     p.add_argument("--copy-calibration", action="store_true",
@@ -150,6 +152,29 @@ def cpu_baseline(cfg, inp, seconds: float):
                       f"{cfg.name} batch, {el:.1f} s wall, numpy fp64 with {threads} BLAS threads"}
 
 
+def graph_replay(L, layers, desc, y, ws, second, K):
+    """The same layer calls (one per cycled layer, no timing events)
+    captured into one HIP graph and replayed: wall time per call."""
+    import torch
+    aux = second.fill(L.MoeAux()) if second is not None else None
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for lay in layers:
+            L.moe_layer(desc, lay.weights, lay.x, y, aux, ws)
+    reps = max(1, K // len(layers))
+    for _ in range(2):
+        g.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        g.replay()
+    torch.cuda.synchronize()
+    per_call = (time.perf_counter() - t0) / (reps * len(layers))
+    del g
+    return {"ms_per_step": round(per_call * 1e3, 4), "value": round(layers[0].cfg.T / per_call, 1),
+            "calls": reps * len(layers)}
+
+
 def main() -> int:
     args = parse()
     if args.traffic:
@@ -250,6 +275,10 @@ def main() -> int:
         if tr.get("kernel_sha") == kernel_hash() and tr.get("workload") == cfg.name:
             roof["traffic"] = tr.get("bytes_per_launch")
 
+    graph = None
+    if args.graph:
+        graph = graph_replay(L, layers, desc, y, ws, second, K)
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(cfg, inputs0, args.cpu_seconds)
@@ -275,6 +304,8 @@ def main() -> int:
         "roofline": roof,
         "cpu_baseline": cpu,
     }
+    if graph is not None:
+        rec["graph_replay"] = graph
     print(json.dumps(rec), flush=True)
     return 0
 

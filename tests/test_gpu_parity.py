@@ -518,6 +518,38 @@ def test_layer_sort_boundary(T):
     assert np.array_equal(U.np_of(t2["sorted_slot"]), np.argsort(flat, kind="stable"))
 
 
+@pytest.mark.parametrize("name", ["longcat_zero_bf16", "dsv3_decode_share_bf16"])
+def test_layer_graph_replay(name):
+    """moe_layer captured into a HIP graph (with the shared expert forked onto
+    a second stream inside the capture where there is one) replays to the
+    eager result bit for bit; new inputs are copied into the captured input
+    buffer between replays, with eager work and synchronisations between."""
+    L, DeviceLayer, to_device = _L()
+    from moe_expert_layer_fp32_amd.layer import SecondStream
+    cfg, inp = U.inputs(name)
+    lay = U.device_layer(name)
+    second = SecondStream() if cfg.shared_inter else None
+    xs = [lay.x.clone(), lay.x.flip(0).contiguous()]
+    eager = [lay.layer(x=xi, second=second) for xi in xs]
+    torch.cuda.synchronize()
+    x_buf, y_buf = xs[0].clone(), torch.empty_like(eager[0])
+    ws = lay.workspace(L.OP_LAYER)
+    U.say(f"[gpu] graph capture {name} streams={2 if second else 1}")
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        lay.layer(x=x_buf, y=y_buf, ws=ws, second=second)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for xi, ye in zip(xs, eager):
+            x_buf.copy_(xi)
+            lay.layer(x=xs[1 - rep % 2])   # eager work between replays
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            assert torch.equal(_bits(y_buf), _bits(ye)), f"replay {rep}"
+    del g
+
+
 def test_layer_largest_k_group_limited():
     """k = 16 (the largest built), group-limited selection of 4 of 8 groups
     over 256 experts, 16 resident, two streams."""
