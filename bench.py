@@ -18,6 +18,7 @@ throughput on a bounded sample of the same workload.
 from __future__ import annotations
 
 import argparse
+import ctypes
 import hashlib
 import json
 import os
@@ -48,6 +49,8 @@ def parse():
     p.add_argument("--layers", type=int, default=0, help="layers cycled (0: enough for > 1 GB of weights)")
     p.add_argument("--cpu-seconds", type=float, default=10.0, help="target CPU time of the oracle sample")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-tune", action="store_true",
+                   help="skip choosing the shared expert's launch limits from measured runs (tuning.py)")
     p.add_argument("--graph", action="store_true",
                    help="also time the same calls replayed from one captured HIP graph (graph_replay)")
     p.add_argument("--streams", type=int, default=2, choices=(1, 2),
@@ -152,11 +155,13 @@ def cpu_baseline(cfg, inp, seconds: float):
                       f"{cfg.name} batch, {el:.1f} s wall, numpy fp64 with {threads} BLAS threads"}
 
 
-def graph_replay(L, layers, desc, y, ws, second, K):
-    """The same layer calls (one per cycled layer, no timing events)
-    captured into one HIP graph and replayed: wall time per call."""
+def graph_replay(L, layers, desc, y, ws, second, K, tuning=None):
+    """The same layer calls (one per cycled layer, no timing events, the same
+    launch limits) captured into one HIP graph and replayed: wall time per call."""
     import torch
     aux = second.fill(L.MoeAux()) if second is not None else None
+    if aux is not None and tuning is not None:
+        aux.tuning = ctypes.pointer(tuning)
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
         for lay in layers:
@@ -241,6 +246,29 @@ def main() -> int:
             second.fill(a)
     warm_aux = second.fill(L.MoeAux()) if second is not None else None
 
+    # Launch limits from measured runs (untimed): only the shared expert on
+    # the second stream has candidates.
+    tuned, t_struct = None, None
+    if second is not None and not args.no_tune:
+        from moe_expert_layer_fp32_amd import tuning as TU
+        bucket = max(TU.load_bucket(c, cfg.ffn_begin, cfg.n_ffn) for c in counts_per_layer)
+        key = TU.shape_key(desc, 2, bucket)
+        cache = TU.TilingCache()
+        tune_aux = second.fill(L.MoeAux())
+
+        def run(t, i):
+            tune_aux.tuning = ctypes.pointer(t) if t is not None else None
+            lay = layers[i % n_layers]
+            L.moe_layer(desc, lay.weights, lay.x, y, tune_aux, ws)
+
+        lim = cache.tune(key, run, torch.cuda.synchronize, calls=max(5, min(20, 4000 // max(1, cfg.T))))
+        t_struct = TU.to_struct(lim)
+        if t_struct is not None:
+            for a in auxes + [warm_aux]:
+                a.tuning = ctypes.pointer(t_struct)
+        tuned = {"limits": lim, "candidates_us": cache.table[key]["us"], "candidate_order": "/".join(TU.FIELDS),
+                 "load_bucket": bucket}
+
     for i in range(W):
         lay = layers[i % n_layers]
         L.moe_layer(desc, lay.weights, lay.x, y, warm_aux, ws)
@@ -277,7 +305,7 @@ def main() -> int:
 
     graph = None
     if args.graph:
-        graph = graph_replay(L, layers, desc, y, ws, second, K)
+        graph = graph_replay(L, layers, desc, y, ws, second, K, t_struct if tuned else None)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -304,6 +332,8 @@ def main() -> int:
         "roofline": roof,
         "cpu_baseline": cpu,
     }
+    if tuned is not None:
+        rec["tuning"] = tuned
     if graph is not None:
         rec["graph_replay"] = graph
     print(json.dumps(rec), flush=True)

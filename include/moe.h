@@ -151,6 +151,28 @@ typedef struct moe_weights {
 } moe_weights;
 
 /*
+ * Launch limits of moe_layer for one layer shape, chosen by the caller from
+ * measured runs: the history-based tiling cache of SwiftGMM (page
+ * "华为技术披露集 VOL.12：昇腾×盘古", section SwiftGMM：专家计算突击队，闪电速度抵达
+ * 推理算力战场) predicts tile parameters from past loads; here the caller
+ * times candidate limits and passes the best (tuning.py keeps such a table).
+ * Each member caps the workgroups one tiled launch of that product may
+ * occupy (all split-K slices together); 0 leaves the library's choice. A cap
+ * only narrows a grid and, for the shared expert, its split of the
+ * reduction, so no cap needs more workspace; a narrower split adds the
+ * partial sums in fewer pieces (results may differ from the uncapped call by
+ * fp32 summation order). Capping the shared expert when it runs on stream2
+ * leaves compute units to the routing kernels it would otherwise crowd out.
+ * Negative members are MOE_ERR_INVALID_ARG. Read during the call only.
+ */
+typedef struct moe_tuning {
+    int32_t shared_ffn1_wgs;  /* shared expert, gate/up projection + SwiGLU */
+    int32_t shared_ffn2_wgs;  /* shared expert, down projection */
+    int32_t routed_ffn1_wgs;  /* routed experts, gate/up projection + SwiGLU */
+    int32_t routed_ffn2_wgs;  /* routed experts, down projection */
+} moe_tuning;
+
+/*
  * Optional outputs and hooks of moe_layer; any NULL member is skipped. The
  * table members, when given, are written instead of workspace copies (same
  * contents as moe_route_topk / moe_permute produce). The events are
@@ -190,6 +212,7 @@ typedef struct moe_aux {
     void* stream2;
     void* ev_fork;
     void* ev_join;
+    const moe_tuning* tuning; /* launch limits (see moe_tuning), or NULL */
 } moe_aux;
 
 /* Workspace bytes an entry point needs for this descriptor (0 if none). */

@@ -76,7 +76,11 @@ struct DensePlan {
   size_t partial_bytes;
 };
 
-DensePlan plan_dense(int M, int N, int K, GemmElem el, int nacc) {
+// cap > 0: at most that many workgroups (a caller's launch limit); it only
+// lowers the split target and the persistent grid, so the plan never needs
+// more split-K workspace than the uncapped one.
+DensePlan plan_dense(int M, int N, int K, GemmElem el, int nacc, int cap = 0) {
+  const int target = cap > 0 ? std::min(cap, TARGET_WGS) : TARGET_WGS;
   DensePlan p{};
   const int ch = lds_chunk_elems(el);
   if (M <= 64 || K % ch != 0 || N % 32 != 0) {
@@ -88,16 +92,16 @@ DensePlan plan_dense(int M, int N, int K, GemmElem el, int nacc) {
   LdsArgs& L = p.L;
   L.tile_rows = M >= 512 ? 128 : 64;
   const int mt = ceil_div(M, L.tile_rows);
-  L.wave_features = (nacc == 1 && N % 256 == 0 && (N / 256) * mt >= TARGET_WGS) ? 64 : 32;
+  L.wave_features = (nacc == 1 && N % 256 == 0 && (N / 256) * mt >= target) ? 64 : 32;
   const int wgs = ceil_div(N, 4 * L.wave_features) * mt;
   const int kc = K / ch;
   int splits = 1;
-  if (wgs < TARGET_WGS) splits = std::max(1, std::min({ceil_div(TARGET_WGS, wgs), kc / 2, MAX_DENSE_SPLITS}));
+  if (wgs < target) splits = std::max(1, std::min({ceil_div(target, wgs), kc / 2, MAX_DENSE_SPLITS}));
   L.splits = splits;
   L.min_rows = 0;
   L.max_rows = INT32_MAX;
   L.part_rows = M;
-  L.max_wgs = PERSISTENT_WGS;
+  L.max_wgs = cap > 0 ? std::min(cap, PERSISTENT_WGS) : PERSISTENT_WGS;
   p.tiles_y = mt;
   p.partial_bytes = splits > 1 ? size_t(splits) * M * nacc * N * 4 : 0;
   return p;
@@ -261,8 +265,10 @@ LayerWs carve_layer(Carve& c, const moe_desc* d) {
 // ---------------------------------------------------------------------------
 // Launch one dense product with its plan (tiled LDS GEMM or streaming).
 moe_status run_dense(GemmArgs g, int M, GemmElem el, int planes, GemmEpi epi, void* partial, hipStream_t s,
-                     KernelEvents ev = {}) {
-  const DensePlan p = plan_dense(M, g.N, g.K, el, epi == EPI_SWIGLU ? 2 : 1);
+                     KernelEvents ev = {}, int cap = 0) {
+  const int nacc = epi == EPI_SWIGLU ? 2 : 1;
+  const DensePlan p = plan_dense(M, g.N, g.K, el, nacc, cap);
+  if (p.partial_bytes > plan_dense(M, g.N, g.K, el, nacc).partial_bytes) return MOE_ERR_INVALID_ARG;
   g.offsets = nullptr;
   g.dense_rows = M;
   g.tiles_y = p.tiles_y;
@@ -286,8 +292,11 @@ moe_status run_dense(GemmArgs g, int M, GemmElem el, int planes, GemmEpi epi, vo
 // workgroups, e.g. 8 resident experts of d 7168) split the reduction over
 // workgroups (routed_splits); shapes that do not tile stream through
 // gemm_rows_kernel, whose wavefronts split the reduction.
+// cap > 0: at most that many workgroups in all (split-K slices included).
+int capped_wgs(int cap, int splits) { return cap > 0 ? std::min(PERSISTENT_WGS, std::max(1, cap / splits)) : PERSISTENT_WGS; }
+
 moe_status run_routed(GemmArgs g, const moe_desc* d, GemmElem el, int planes, GemmEpi epi, void* partial,
-                      hipStream_t s, KernelEvents ev = {}) {
+                      hipStream_t s, KernelEvents ev = {}, int cap = 0) {
   const int splits = routed_splits(d, g.N, g.K);
   if (splits > 1) {
     LdsArgs L{};
@@ -295,7 +304,7 @@ moe_status run_routed(GemmArgs g, const moe_desc* d, GemmElem el, int planes, Ge
     L.splits = splits;
     L.partial = partial;
     L.part_rows = r_max(d);
-    L.max_wgs = PERSISTENT_WGS;
+    L.max_wgs = capped_wgs(cap, splits);
     L.tile_rows = 64;
     L.min_rows = 1;
     L.max_rows = INT32_MAX;
@@ -309,7 +318,7 @@ moe_status run_routed(GemmArgs g, const moe_desc* d, GemmElem el, int planes, Ge
     L.wave_features = 32;
     L.splits = 1;
     L.part_rows = r_max(d);
-    L.max_wgs = PERSISTENT_WGS;
+    L.max_wgs = capped_wgs(cap, 1);
     L.tile_rows = 64;
     L.min_rows = 1;
     L.max_rows = d->T >= PREFILL_T ? 64 : INT32_MAX;
@@ -413,7 +422,14 @@ struct FfnPlan {
   int first;
   const int32_t* sorted_slot;  // routed only
   int rows_bound;              // routed: r_max; shared: T
+  int cap1 = 0, cap2 = 0;      // workgroup caps of the two products (0: none)
 };
+// The plan with the caller's launch limits for these products applied.
+FfnPlan with_caps(FfnPlan p, int cap1, int cap2) {
+  p.cap1 = cap1;
+  p.cap2 = cap2;
+  return p;
+}
 
 moe_status run_ffn(const moe_desc* d, const FfnPlan& p, const void* x, const FfnWs& f, void* rows, bool rows_bf16,
                    hipStream_t s, hipEvent_t e1b, hipEvent_t e1e, hipEvent_t e2b, hipEvent_t e2e) {
@@ -444,8 +460,8 @@ moe_status run_ffn(const moe_desc* d, const FfnPlan& p, const void* x, const Ffn
   g1.ldo = size_t(p.inter) * h_bytes(d);
   g1.out_bf16 = d->dtype == MOE_DTYPE_BF16;
   const KernelEvents ev1{e1b, e1e}, ev2{e2b, e2e};
-  st = routed ? run_routed(g1, d, el, 2, EPI_SWIGLU, f.partial, s, ev1)
-              : run_dense(g1, d->T, el, 2, EPI_SWIGLU, f.partial, s, ev1);
+  st = routed ? run_routed(g1, d, el, 2, EPI_SWIGLU, f.partial, s, ev1, p.cap1)
+              : run_dense(g1, d->T, el, 2, EPI_SWIGLU, f.partial, s, ev1, p.cap1);
   if (st != MOE_OK) return st;
 
   if (w8a8(d)) {
@@ -470,8 +486,8 @@ moe_status run_ffn(const moe_desc* d, const FfnPlan& p, const void* x, const Ffn
   g2.out = static_cast<uint8_t*>(rows);
   g2.ldo = size_t(d->d) * (rows_bf16 ? 2 : 4);
   g2.out_bf16 = rows_bf16;
-  st = routed ? run_routed(g2, d, el, 1, EPI_SUM, f.partial, s, ev2)
-              : run_dense(g2, d->T, el, 1, EPI_SUM, f.partial, s, ev2);
+  st = routed ? run_routed(g2, d, el, 1, EPI_SUM, f.partial, s, ev2, p.cap2)
+              : run_dense(g2, d->T, el, 1, EPI_SUM, f.partial, s, ev2, p.cap2);
   if (st != MOE_OK) return st;
   return MOE_OK;
 }
@@ -685,6 +701,9 @@ moe_status moe_layer(const moe_desc* d, const moe_weights* w, const void* x, voi
     const int given = !!aux->stream2 + !!aux->ev_fork + !!aux->ev_join;
     if (given != 0 && given != 3) return MOE_ERR_INVALID_ARG;
     if (aux->stream2 && aux->stream2 == stream) return MOE_ERR_INVALID_ARG;
+    const moe_tuning* t = aux->tuning;
+    if (t && (t->shared_ffn1_wgs < 0 || t->shared_ffn2_wgs < 0 || t->routed_ffn1_wgs < 0 || t->routed_ffn2_wgs < 0))
+      return MOE_ERR_INVALID_ARG;
   }
   const size_t need = ws_bytes_of(d, MOE_OP_LAYER);
   if (ws_bytes < need || !ws) return MOE_ERR_WORKSPACE;
@@ -700,6 +719,9 @@ moe_status moe_layer(const moe_desc* d, const moe_weights* w, const void* x, voi
   int32_t* offsets = A.offsets ? A.offsets : L.offsets;
   int32_t* sorted_slot = A.sorted_slot ? A.sorted_slot : L.sorted_slot;
   int32_t* slot_pos = A.slot_pos ? A.slot_pos : L.slot_pos;
+  const moe_tuning tune = A.tuning ? *A.tuning : moe_tuning{};
+  auto shared_caps = [&](const FfnPlan& p) { return with_caps(p, tune.shared_ffn1_wgs, tune.shared_ffn2_wgs); };
+  auto routed_caps = [&](const FfnPlan& p) { return with_caps(p, tune.routed_ffn1_wgs, tune.routed_ffn2_wgs); };
   if (A.q_x) L.routed.qx = L.shared.qx = A.q_x;
   if (A.s_x) L.routed.sx = L.shared.sx = A.s_x;
 
@@ -714,7 +736,8 @@ moe_status moe_layer(const moe_desc* d, const moe_weights* w, const void* x, voi
     hipStream_t s2 = static_cast<hipStream_t>(A.stream2);
     HIP_TRY(hipEventRecord(static_cast<hipEvent_t>(A.ev_fork), s));
     HIP_TRY(hipStreamWaitEvent(s2, static_cast<hipEvent_t>(A.ev_fork), 0));
-    st = run_ffn(d, shared_plan(d, w), x, L.shared, L.shared_rows, rb, s2, nullptr, nullptr, nullptr, nullptr);
+    st = run_ffn(d, shared_caps(shared_plan(d, w)), x, L.shared, L.shared_rows, rb, s2, nullptr, nullptr, nullptr,
+                 nullptr);
     if (st != MOE_OK) return st;
     HIP_TRY(hipEventRecord(static_cast<hipEvent_t>(A.ev_join), s2));
   }
@@ -725,7 +748,7 @@ moe_status moe_layer(const moe_desc* d, const moe_weights* w, const void* x, voi
   HIP_TRY(launch_permute(idx, d->T * d->k, d->E, counts, offsets, sorted_slot, slot_pos, L.chunk_hist, s));
   if (d->T == 0) return MOE_OK;
   if (d->n_ffn > 0) {
-    st = run_ffn(d, routed_plan(d, w, offsets, sorted_slot), x, L.routed, L.rows, rb, s,
+    st = run_ffn(d, routed_caps(routed_plan(d, w, offsets, sorted_slot)), x, L.routed, L.rows, rb, s,
                  static_cast<hipEvent_t>(A.ev_ffn1_begin), static_cast<hipEvent_t>(A.ev_ffn1_end),
                  static_cast<hipEvent_t>(A.ev_ffn2_begin), static_cast<hipEvent_t>(A.ev_ffn2_end));
     if (st != MOE_OK) return st;
@@ -733,7 +756,8 @@ moe_status moe_layer(const moe_desc* d, const moe_weights* w, const void* x, voi
   if (fork) {
     HIP_TRY(hipStreamWaitEvent(s, static_cast<hipEvent_t>(A.ev_join), 0));
   } else if (d->shared_inter > 0) {
-    st = run_ffn(d, shared_plan(d, w), x, L.shared, L.shared_rows, rb, s, nullptr, nullptr, nullptr, nullptr);
+    st = run_ffn(d, shared_caps(shared_plan(d, w)), x, L.shared, L.shared_rows, rb, s, nullptr, nullptr, nullptr,
+                 nullptr);
     if (st != MOE_OK) return st;
   }
   const CombineArgs cb = combine_args(d, x, L.rows, L.shared_rows, rb, idx, tw, offsets, slot_pos, y);

@@ -6,6 +6,8 @@ kernels behind the C ABI.
 """
 from __future__ import annotations
 
+import ctypes
+
 import numpy as np
 import torch
 
@@ -140,18 +142,24 @@ class DeviceLayer:
         L.moe_combine(self.desc_for(T), x, rows, shared_rows, topk_idx, topk_w, offsets, slot_pos, y)
         return y
 
-    def layer(self, x=None, y=None, aux: L.MoeAux | None = None, ws=None, second: SecondStream | None = None):
-        """moe_layer; with `second`, the shared expert runs on its stream."""
+    def layer(self, x=None, y=None, aux: L.MoeAux | None = None, ws=None, second: SecondStream | None = None,
+              tuning: L.MoeTuning | None = None):
+        """moe_layer; with `second`, the shared expert runs on its stream;
+        `tuning`: launch limits (moe_tuning)."""
         x = self.x if x is None else x
         T = x.shape[0]
         y = torch.empty((T, self.cfg.d), dtype=self.xdtype, device=self.device) if y is None else y
         ws = self.workspace(L.OP_LAYER, T) if ws is None else ws
         if second is not None:
             aux = second.fill(L.MoeAux() if aux is None else aux)
+        if tuning is not None:
+            aux = L.MoeAux() if aux is None else aux
+            aux.tuning = ctypes.pointer(tuning)
         L.moe_layer(self.desc_for(T), self.weights, x, y, aux, ws)
         return y
 
-    def layer_with_tables(self, x=None, ws=None):
+    def layer_with_tables(self, x=None, ws=None, second: SecondStream | None = None,
+                          tuning: L.MoeTuning | None = None):
         """moe_layer plus its routing tables (and W8A8 activation codes) via moe_aux."""
         x = self.x if x is None else x
         T, k, E, dev = x.shape[0], self.cfg.k, self.cfg.E, self.device
@@ -165,5 +173,5 @@ class DeviceLayer:
             t["q_x"] = torch.empty((T, self.cfg.d), dtype=torch.int8, device=dev)
             t["s_x"] = torch.empty(T, dtype=torch.float32, device=dev)
         aux = L.MoeAux(**{n: L.ptr(v) for n, v in t.items()})
-        y = self.layer(x, aux=aux, ws=ws)
+        y = self.layer(x, aux=aux, ws=ws, second=second, tuning=tuning)
         return y, t

@@ -53,11 +53,16 @@ class MoeWeights(ctypes.Structure):
                 ("s2", _vp), ("sw13", _vp), ("sw2", _vp), ("ss1", _vp), ("ss3", _vp), ("ss2", _vp)]
 
 
+class MoeTuning(ctypes.Structure):
+    _fields_ = [("shared_ffn1_wgs", ctypes.c_int32), ("shared_ffn2_wgs", ctypes.c_int32),
+                ("routed_ffn1_wgs", ctypes.c_int32), ("routed_ffn2_wgs", ctypes.c_int32)]
+
+
 class MoeAux(ctypes.Structure):
     _fields_ = [("topk_idx", _vp), ("topk_w", _vp), ("counts", _vp), ("offsets", _vp), ("sorted_slot", _vp),
                 ("slot_pos", _vp), ("q_x", _vp), ("s_x", _vp), ("ev_ffn1_begin", _vp), ("ev_ffn1_end", _vp),
                 ("ev_ffn2_begin", _vp), ("ev_ffn2_end", _vp), ("stream2", _vp), ("ev_fork", _vp),
-                ("ev_join", _vp)]
+                ("ev_join", _vp), ("tuning", ctypes.POINTER(MoeTuning))]
 
 
 _lib_handle = None

@@ -1,0 +1,110 @@
+"""Launch limits for moe_layer chosen from measured runs.
+
+This is the history-based tiling cache of SwiftGMM (page "华为技术披露集
+VOL.12：昇腾×盘古", section SwiftGMM：专家计算突击队，闪电速度抵达推理算力战场):
+tile parameters are predicted from past loads instead of being fixed. Here
+the parameters are the workgroup caps of moe_tuning. For one layer shape and
+one bucket of its per-expert token counts, a few candidate caps are timed on
+the caller's own layer calls, and the fastest is kept in a host-side table.
+The table is keyed by plain values and can be saved to JSON and loaded back.
+A serving loop takes the bucket from the counts of its previous call
+(moe_aux.counts), so choosing an entry never waits for the device.
+
+The caps matter where the shared expert runs on a second stream: its
+persistent GEMMs can occupy every compute unit while the router, gate and
+permutation of the same call wait for room. Capping it leaves units free
+for them. Whether that pays depends on the shape, so it is measured rather
+than modelled.
+"""
+from __future__ import annotations
+
+import json
+import math
+import time
+from typing import Callable
+
+import numpy as np
+
+from . import lib as L
+
+FIELDS = ("shared_ffn1_wgs", "shared_ffn2_wgs", "routed_ffn1_wgs", "routed_ffn2_wgs")
+
+# Candidate caps (shared gate/up, shared down); the routed launches keep the
+# library's grids. (0, 0) is the library's own choice and always a candidate.
+SHARED_CANDIDATES = ((0, 0), (96, 0), (128, 0), (192, 0), (128, 128), (192, 192))
+
+
+def limits(shared_ffn1_wgs=0, shared_ffn2_wgs=0, routed_ffn1_wgs=0, routed_ffn2_wgs=0) -> dict:
+    return dict(zip(FIELDS, (shared_ffn1_wgs, shared_ffn2_wgs, routed_ffn1_wgs, routed_ffn2_wgs)))
+
+
+def label(lim: dict) -> str:
+    """Short name of a limits dict: the four caps in FIELDS order."""
+    return "/".join(str(int(lim.get(f, 0))) for f in FIELDS)
+
+
+def to_struct(lim: dict | None) -> L.MoeTuning | None:
+    """moe_tuning for a limits dict (None: no limits)."""
+    if lim is None or not any(lim.values()):
+        return None
+    return L.MoeTuning(**{f: int(lim.get(f, 0)) for f in FIELDS})
+
+
+def load_bucket(counts, ffn_begin: int, n_ffn: int) -> int:
+    """Bucket of the per-expert token counts of the resident FFN experts:
+    ceil(log2(1 + largest count)), which fixes how many row tiles the
+    largest expert needs."""
+    c = np.asarray(counts)[ffn_begin:ffn_begin + n_ffn]
+    return int(math.ceil(math.log2(1 + int(c.max())))) if c.size else 0
+
+
+def shape_key(desc: L.MoeDesc, streams: int, bucket: int) -> str:
+    """Table key: the layer shape, the number of streams and the load bucket."""
+    parts = [f"{f}={getattr(desc, f)}" for f in ("T", "d", "E", "k", "n_ffn", "n_zero", "inter", "shared_inter",
+                                                 "dtype", "gate", "n_group", "topk_group", "per_group_k")]
+    return ",".join(parts + [f"streams={streams}", f"bucket={bucket}"])
+
+
+class TilingCache:
+    """Host-side table: key -> {"limits": {...}, "us": {label(candidate): time}}."""
+
+    def __init__(self, table: dict | None = None):
+        self.table = dict(table or {})
+
+    def lookup(self, key: str) -> dict | None:
+        e = self.table.get(key)
+        return None if e is None else dict(e["limits"])
+
+    def tune(self, key: str, run: Callable[[L.MoeTuning | None, int], None], sync: Callable[[], None],
+             candidates=SHARED_CANDIDATES, calls: int = 20, reps: int = 3) -> dict:
+        """Time every candidate and keep the fastest for `key`. run(tuning, i)
+        enqueues the i-th layer call with that moe_tuning; sync() waits for the
+        device. Each candidate's time is the best over `reps` rounds of
+        `calls` calls (the calls are device-bound, so wall time between two
+        synchronisations is device time)."""
+        cands = {label(lim): lim for lim in (limits(*c) for c in candidates)}
+        times: dict[str, float] = {}
+        for _ in range(reps):
+            for name, lim in cands.items():
+                t = to_struct(lim)
+                for i in range(3):
+                    run(t, i)
+                sync()
+                t0 = time.perf_counter()
+                for i in range(calls):
+                    run(t, i)
+                sync()
+                us = (time.perf_counter() - t0) / calls * 1e6
+                times[name] = min(us, times.get(name, math.inf))
+        best = min(times, key=times.get)
+        self.table[key] = {"limits": dict(cands[best]), "us": {k: round(v, 2) for k, v in times.items()}}
+        return dict(cands[best])
+
+    def save(self, path: str) -> None:
+        with open(path, "w") as f:
+            json.dump(self.table, f, indent=1, sort_keys=True)
+
+    @classmethod
+    def load(cls, path: str) -> "TilingCache":
+        with open(path) as f:
+            return cls(json.load(f))

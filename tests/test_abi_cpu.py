@@ -6,6 +6,7 @@ from __future__ import annotations
 import ctypes
 import os
 import re
+import subprocess
 
 import pytest
 
@@ -38,11 +39,29 @@ def test_library_exports_every_declared_function(L):
         assert hasattr(lib, name), name
 
 
-def test_struct_sizes_match_header(L):
-    # 16 int32 + 1 float; 12 pointers; 15 pointers
-    assert ctypes.sizeof(L.MoeDesc) == 17 * 4
-    assert ctypes.sizeof(L.MoeWeights) == 12 * 8
-    assert ctypes.sizeof(L.MoeAux) == 15 * 8
+def test_struct_layouts_match_header(L, tmp_path):
+    """Size and member offsets of every ctypes struct of the binding equal
+    what a C compiler makes of moe.h."""
+    structs = {"moe_desc": L.MoeDesc, "moe_weights": L.MoeWeights, "moe_aux": L.MoeAux,
+               "moe_tuning": L.MoeTuning}
+    lines = ["#include <stdio.h>", "#include <stddef.h>", '#include "moe.h"', "int main(void) {"]
+    for cname, py in structs.items():
+        lines.append(f'printf("{cname} sizeof %zu\\n", sizeof({cname}));')
+        lines += [f'printf("{cname} {f} %zu\\n", offsetof({cname}, {f}));' for f, _ in py._fields_]
+    lines.append("return 0; }")
+    src, exe = tmp_path / "layout.c", tmp_path / "layout"
+    src.write_text("\n".join(lines))
+    subprocess.run(["gcc", "-std=c11", "-Wall", "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)],
+                   check=True)
+    out = subprocess.run([str(exe)], capture_output=True, text=True, check=True).stdout.split("\n")
+    checked = 0
+    for line in filter(None, out):
+        cname, field, val = line.split()
+        py = structs[cname]
+        want = ctypes.sizeof(py) if field == "sizeof" else getattr(py, field).offset
+        assert int(val) == want, line
+        checked += 1
+    assert checked == sum(len(py._fields_) + 1 for py in structs.values())
 
 
 def test_status_strings(L):
@@ -140,6 +159,21 @@ def test_second_stream_needs_both_events(L):
                              stream) == -1, given
     # all three given: validation passes and only the workspace check fails
     aux = L.MoeAux(stream2=FAKE, ev_fork=FAKE, ev_join=FAKE)
+    assert lib.moe_layer(ctypes.byref(d), ctypes.byref(w), FAKE, FAKE, ctypes.byref(aux), FAKE, 0, None) == -3
+
+
+def test_negative_launch_limit_rejected(L):
+    d = _desc(L)
+    lib = L.load_library()
+    w = L.MoeWeights(router=FAKE, w13=FAKE, w2=FAKE, sw13=FAKE, sw2=FAKE)
+    for field in ("shared_ffn1_wgs", "shared_ffn2_wgs", "routed_ffn1_wgs", "routed_ffn2_wgs"):
+        t = L.MoeTuning(**{field: -1})
+        aux = L.MoeAux(tuning=ctypes.pointer(t))
+        assert lib.moe_layer(ctypes.byref(d), ctypes.byref(w), FAKE, FAKE, ctypes.byref(aux), FAKE, 1 << 40,
+                             None) == -1, field
+    # zero and positive limits pass validation; only the workspace check fails
+    t = L.MoeTuning(shared_ffn1_wgs=128, routed_ffn2_wgs=0)
+    aux = L.MoeAux(tuning=ctypes.pointer(t))
     assert lib.moe_layer(ctypes.byref(d), ctypes.byref(w), FAKE, FAKE, ctypes.byref(aux), FAKE, 0, None) == -3
 
 

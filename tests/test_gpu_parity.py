@@ -381,8 +381,8 @@ LAYER_CASES = [("tiny_fp32", None), ("tiny_fp32", 333), ("longcat_zero_bf16", No
                ("dsv3_decode_share_bf16", None), ("dsv3_decode_share_bf16", 129), ("pangu_moge_w8a8", None)]
 
 
-def _check_layer(cfg, inp, lay, tokens=None, ws=None):
-    y, t = lay.layer_with_tables(ws=ws)
+def _check_layer(cfg, inp, lay, tokens=None, ws=None, second=None, tuning=None):
+    y, t = lay.layer_with_tables(ws=ws, second=second, tuning=tuning)
     torch.cuda.synchronize()
     idx_gpu, w_gpu = U.np_of(t["topk_idx"]), U.np_of(t["topk_w"])
     ref = O.moe_layer(inp, cfg, tokens=tokens)
@@ -548,6 +548,29 @@ def test_layer_graph_replay(name):
             torch.cuda.synchronize()
             assert torch.equal(_bits(y_buf), _bits(ye)), f"replay {rep}"
     del g
+
+
+@pytest.mark.parametrize("name,caps", [("dsv3_decode_share_bf16", (128, 128, 0, 0)),
+                                       ("pangu_moge_w8a8", (96, 192, 64, 40)),
+                                       ("longcat_zero_bf16", (0, 0, 1, 8))])
+def test_layer_launch_limits(name, caps):
+    """moe_layer under workgroup caps (moe_tuning), with the shared expert on
+    a second stream: narrower persistent grids and splits of the reduction,
+    down to the smallest grid (a cap of 1), still match the oracle and give
+    the same routing tables."""
+    L, DeviceLayer, to_device = _L()
+    from moe_expert_layer_fp32_amd.layer import SecondStream
+    from moe_expert_layer_fp32_amd import tuning as TU
+    cfg, inp = U.inputs(name)
+    lay = U.device_layer(name)
+    t = TU.to_struct(TU.limits(*caps))
+    U.say(f"[gpu] layer {name} launch limits {caps}")
+    second = SecondStream() if cfg.shared_inter else None
+    y = _check_layer(cfg, inp, lay, second=second, tuning=t)
+    y0 = lay.layer(second=second)
+    torch.cuda.synchronize()
+    _, dev = U.output_errors(U.np_of(y), U.np_of(y0).astype(np.float64), cfg.dtype)
+    U.record(test="layer_launch_limits", cfg=name, caps=list(caps), err_vs_uncapped=dev)
 
 
 def test_layer_largest_k_group_limited():
