@@ -293,9 +293,19 @@ moe_status moe_combine(const moe_desc* desc, const void* x, const float* rows,
                        const int32_t* slot_pos, void* y, void* stream);
 
 /*
- * The whole layer: route_topk -> permute -> (W8A8: quantise x) -> routed
- * FFN -> shared FFN -> combine, in one call. x: [T][d]; y: [T][d] (types as
- * in moe_combine). aux may be NULL.
+ * The whole layer in one call: (W8A8: quantise x) -> route_topk -> permute
+ * -> routed FFN -> shared FFN (on aux->stream2 when given, overlapping the
+ * rest) -> combine. x: [T][d]; y: [T][d] (types as in moe_combine). aux may
+ * be NULL. The arithmetic is that of the separate entry points, except that
+ * the bf16 layer keeps the expert output rows in bf16 between the down
+ * projection and the combine (the sum over experts still runs in fp32; fp32
+ * and W8A8 layers keep fp32 rows), and that launch limits (aux->tuning) may
+ * change how the shared expert splits its reductions (fp32 summation order
+ * only). Errors: those of the separate entry points, MOE_ERR_INVALID_ARG for
+ * an incomplete stream2/ev_fork/ev_join triple, stream2 equal to stream, or
+ * a negative launch limit, and MOE_ERR_WORKSPACE when ws_bytes is below
+ * moe_workspace_bytes(desc, MOE_OP_LAYER); these are returned before
+ * anything is launched.
  */
 moe_status moe_layer(const moe_desc* desc, const moe_weights* w, const void* x,
                      void* y, moe_aux* aux, void* ws, size_t ws_bytes,

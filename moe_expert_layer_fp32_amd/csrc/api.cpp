@@ -231,7 +231,7 @@ struct LayerWs {
   int32_t* chunk_hist;
   float* w;
   FfnWs routed, shared;
-  void *rows, *shared_rows;   // expert outputs: bf16 for bf16 / W8A8 layers, else fp32
+  void *rows, *shared_rows;   // expert outputs: bf16 in the bf16 layer, else fp32 (layer_row_bytes)
 };
 LayerWs carve_layer(Carve& c, const moe_desc* d) {
   LayerWs L{};
