@@ -96,7 +96,6 @@ __device__ inline bool locate_tile(const GemmArgs& a, int tile, int& g, int& row
   return true;
 }
 
-__device__ inline float silu(float v) { return v / (1.0f + expf(-v)); }
 
 // One wavefront's 16 output columns of one m-tile with MB row blocks, over
 // the reduction steps [kt0, kt1). Operands are software-pipelined D steps
@@ -217,7 +216,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int g, int row0, in
       if (EPI == EPI_SWIGLU) {
         const float ga = Tr::to_f32(acc[0][mb], j) * bsc * cs0[j];
         const float up = Tr::to_f32(acc[1][mb], j) * bsc * cs1[j];
-        v[j] = silu(ga) * up;
+        v[j] = silu_f(ga) * up;
       } else {
         v[j] = Tr::to_f32(acc[0][mb], j) * bsc * cs0[j] + bias[j];
       }

@@ -7,8 +7,6 @@
 
 namespace moe {
 
-__device__ inline float silu_f(float v) { return v / (1.0f + expf(-v)); }
-
 // Locate m-tile `tile` (rows per tile `tm`) among the groups whose row count
 // lies in [lo, hi]. Wave-uniform; false past the last tile.
 __device__ inline bool locate_tile_lds(const GemmArgs& a, int tile, int tm, int lo, int hi, int& g, int& row0,
