@@ -35,6 +35,7 @@ struct M32BF16 {
   using acc_t = f32x16;
   using part_t = float;
   static constexpr int KF = 32, KM = 16, BPL = 16, ESZ = 2;
+  static constexpr bool SCALED = false;   // no per-row / per-column scales
   __device__ static inline acc_t mfma(op_t a, op_t b, acc_t c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
   }
@@ -47,6 +48,7 @@ struct M32I8 {
   using acc_t = i32x16;
   using part_t = int;
   static constexpr int KF = 64, KM = 32, BPL = 16, ESZ = 1;
+  static constexpr bool SCALED = true;    // int8 codes: activation-row and weight-column scales
   __device__ static inline acc_t mfma(op_t a, op_t b, acc_t c) {
     return __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, c, 0, 0, 0);
   }
@@ -59,6 +61,7 @@ struct M32F32 {
   using acc_t = f32x16;
   using part_t = float;
   static constexpr int KF = 4, KM = 2, BPL = 4, ESZ = 4;
+  static constexpr bool SCALED = false;
   __device__ static inline acc_t mfma(op_t a, op_t b, acc_t c) {
     return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
   }
@@ -120,9 +123,42 @@ __device__ __forceinline__ void gemm_lds_tile(const GemmArgs& a, const LdsArgs& 
   };
 
 
+  // ---- epilogue operands that depend on columns only, loaded now so their
+  // latency hides under the main loop (none for unscaled, bias-free products;
+  // a load in the epilogue would also wait for every load still in flight) ----
+  const bool final_out = L.splits == 1;   // split-K slices write raw partial sums
+  // int8 weight scales of columns c0..c0+3; the widest int8 tile (64
+  // features, 128 rows) has no registers to spare and reads them at the end
+  constexpr bool EARLY_CS = Tr::SCALED && !(NF == 64 && BM == 128);
+  f32x4 ep_cs[NACC][FT][4];
+  f32x4 ep_bias[FT][4];                   // sums: logit bias of columns c0..c0+3 (0 past n_valid)
+#pragma unroll
+  for (int f = 0; f < FT; ++f)
+#pragma unroll
+    for (int jg = 0; jg < 4; ++jg) {
+      const int c0 = (ft0 + f) * 32 + 8 * jg + 4 * half;
+#pragma unroll
+      for (int s = 0; s < NACC; ++s) {
+        ep_cs[s][f][jg] = f32x4{1.f, 1.f, 1.f, 1.f};
+        const float* sp = s == 0 ? a.a_scale0 : a.a_scale1;
+        if constexpr (EARLY_CS)
+          if (final_out && sp) ep_cs[s][f][jg] = *reinterpret_cast<const f32x4*>(sp + size_t(g) * a.a_scale_stride + c0);
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        ep_bias[f][jg][j] = 0.f;
+        if constexpr (EPI == EPI_SUM)
+          if (final_out && a.bias && c0 + j < a.n_valid) ep_bias[f][jg][j] = a.bias[c0 + j];
+      }
+    }
+
   // ---- B staging: this thread's rows and byte column inside a chunk ----
+  // (int8: the threads at byte column 0 also fetch their row's activation
+  // scale, which reaches the epilogue's lanes through LDS)
+  __shared__ float bs_lds[BM];
   const uint8_t* bsrc[LOADS];
   int bdst[LOADS];
+  float bsv[LOADS];
 #pragma unroll
   for (int i = 0; i < LOADS; ++i) {
     const int lin = threadIdx.x + i * WG_THREADS;
@@ -132,7 +168,13 @@ __device__ __forceinline__ void gemm_lds_tile(const GemmArgs& a, const LdsArgs& 
     const int brow = a.sorted_slot ? a.sorted_slot[row0 + rr] / a.k : out0 + rr;
     bsrc[i] = a.B + size_t(brow) * a.ldb + size_t(c_begin) * CH_BYTES + col;
     bdst[i] = r * LDS_ROW + col;
+    bsv[i] = 1.f;
+    if constexpr (Tr::SCALED)
+      if (final_out && a.b_scale && col == 0) bsv[i] = a.b_scale[brow];
   }
+  float ep_bs[MBK];   // activation scale of epilogue row m * 32 + r32
+#pragma unroll
+  for (int m = 0; m < MBK; ++m) ep_bs[m] = 1.f;
   // Two register stages of chunk loads (parity of the chunk index).
   u32x4 bstage[2][LOADS];
   auto load_b = [&](int st, int c) {
@@ -203,7 +245,19 @@ __device__ __forceinline__ void gemm_lds_tile(const GemmArgs& a, const LdsArgs& 
     for (int r = 0; r < RA; ++r) load_a(r, min(r, nsteps - 1));
     store_b(0, 0);
     load_b(0, min(2, nch - 1));
+    if constexpr (Tr::SCALED) {
+#pragma unroll
+      for (int i = 0; i < LOADS; ++i) {
+        const int lin = threadIdx.x + i * WG_THREADS;
+        if (lin % (CH_BYTES / 16) == 0) bs_lds[lin / (CH_BYTES / 16)] = bsv[i];
+      }
+    }
     __syncthreads();
+    // read before the chunk barriers below, so the next tile may rewrite bs_lds
+    if constexpr (Tr::SCALED) {
+#pragma unroll
+      for (int m = 0; m < MBK; ++m) ep_bs[m] = bs_lds[m * 32 + r32];
+    }
     // chunk c stores chunk c + 1 from stage (c + 1) & 1
     int c = 0;
     for (; c + 2 <= nch; c += 2) {
@@ -221,11 +275,7 @@ __device__ __forceinline__ void gemm_lds_tile(const GemmArgs& a, const LdsArgs& 
     const int r = m * 32 + r32;
     if (r >= nrows) continue;
     const int orow = out0 + r;
-    float bs = 1.f;
-    if (L.splits == 1 && a.b_scale) {
-      const int brow = a.sorted_slot ? a.sorted_slot[row0 + r] / a.k : orow;
-      bs = a.b_scale[brow];
-    }
+    const float bs = ep_bs[m];
 #pragma unroll
     for (int f = 0; f < FT; ++f) {
 #pragma unroll
@@ -244,18 +294,24 @@ __device__ __forceinline__ void gemm_lds_tile(const GemmArgs& a, const LdsArgs& 
           }
           continue;
         }
+        if constexpr (Tr::SCALED && !EARLY_CS) {
+#pragma unroll
+          for (int s = 0; s < NACC; ++s) {
+            const float* sp = s == 0 ? a.a_scale0 : a.a_scale1;
+            if (sp) ep_cs[s][f][jg] = *reinterpret_cast<const f32x4*>(sp + size_t(g) * a.a_scale_stride + c0);
+          }
+        }
         float v[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const float cs0 = a.a_scale0 ? a.a_scale0[size_t(g) * a.a_scale_stride + c0 + j] : 1.f;
+          const float cs0 = ep_cs[0][f][jg][j];
           if (EPI == EPI_SWIGLU) {
-            const float cs1 = a.a_scale1 ? a.a_scale1[size_t(g) * a.a_scale_stride + c0 + j] : 1.f;
+            const float cs1 = ep_cs[NACC - 1][f][jg][j];
             const float ga = float(acc[0][f][m][jg * 4 + j]) * bs * cs0;
             const float up = float(acc[1][f][m][jg * 4 + j]) * bs * cs1;
             v[j] = silu_f(ga) * up;
           } else {
-            const float bias = (a.bias && c0 + j < a.n_valid) ? a.bias[c0 + j] : 0.f;
-            v[j] = float(acc[0][f][m][jg * 4 + j]) * bs * cs0 + bias;
+            v[j] = float(acc[0][f][m][jg * 4 + j]) * bs * cs0 + ep_bias[f][jg][j];
           }
         }
         uint8_t* op = a.out + size_t(orow) * a.ldo;
