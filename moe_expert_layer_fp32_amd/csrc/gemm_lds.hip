@@ -344,7 +344,9 @@ template <class Tr, int S, int EPI, int NF, int BM>
 __global__ __launch_bounds__(WG_THREADS) __attribute__((amdgpu_waves_per_eu(lds_waves_per_eu<Tr, S, EPI, NF, BM>())))
 void gemm_lds_kernel(GemmArgs a, LdsArgs L) {
   __shared__ __attribute__((aligned(16))) uint8_t lds[2][BM * LDS_ROW];
-  const int tiles = count_tiles_lds(a, BM, L.min_rows, L.max_rows);
+  __shared__ int offs[TILE_MAX_GROUPS + 1];
+  stage_offsets(a, offs);
+  const int tiles = count_tiles_lds(a, offs, BM, L.min_rows, L.max_rows);
   const int nblocks = ceil_div(a.N, WG_WAVES * NF);
   const int total = tiles * nblocks;
   const int nwg = gridDim.x;
@@ -355,7 +357,7 @@ void gemm_lds_kernel(GemmArgs a, LdsArgs L) {
     const int tile = logical % tiles;
     const int nblock = logical / tiles;
     int g, row0, nrows, out0;
-    if (!locate_tile_lds(a, tile, BM, L.min_rows, L.max_rows, g, row0, nrows, out0)) break;
+    if (!locate_tile_lds(a, offs, tile, BM, L.min_rows, L.max_rows, g, row0, nrows, out0)) break;
     g = __builtin_amdgcn_readfirstlane(g);
     row0 = __builtin_amdgcn_readfirstlane(row0);
     nrows = __builtin_amdgcn_readfirstlane(nrows);
@@ -479,6 +481,7 @@ static hipError_t launch_lds_shape(const GemmArgs& a, const LdsArgs& L, hipStrea
 
 hipError_t launch_gemm_lds(const GemmArgs& a, const LdsArgs& L, GemmElem elem, int planes, GemmEpi epi,
                            hipStream_t stream, KernelEvents ev) {
+  if (a.offsets && (a.n_groups < 1 || a.n_groups > TILE_MAX_GROUPS)) return hipErrorInvalidValue;
   if (a.tiles_y <= 0) return record_events(ev.start, ev.stop, stream);
   if (epi == EPI_SWIGLU) {
     switch (elem) {

@@ -1,5 +1,5 @@
-// Device-side tile bookkeeping shared by the tiled matrix-core kernels:
-// locating the m-tiles of row groups (experts) from the routing offsets.
+// Device-side tile bookkeeping of the tiled matrix-core kernel: locating the
+// m-tiles of row groups (experts) from the routing offsets.
 #pragma once
 
 #include "common.h"
@@ -7,10 +7,41 @@
 
 namespace moe {
 
-// Locate m-tile `tile` (rows per tile `tm`) among the groups whose row count
-// lies in [lo, hi]. Wave-uniform; false past the last tile.
-__device__ inline bool locate_tile_lds(const GemmArgs& a, int tile, int tm, int lo, int hi, int& g, int& row0,
-                                       int& nrows, int& out0) {
+constexpr int TILE_MAX_GROUPS = 256;   // 4 groups per lane of one wavefront
+
+// The routing offsets of the groups [first, first + n_groups] copied into
+// LDS once per workgroup (one global round trip); every later tile lookup
+// reads only LDS. All threads of the workgroup call it; null offsets
+// (a dense product) copy nothing.
+__device__ inline void stage_offsets(const GemmArgs& a, int* offs) {
+  if (a.offsets == nullptr) return;
+  for (int i = threadIdx.x; i <= a.n_groups; i += blockDim.x) offs[i] = a.offsets[a.first + i];
+  __syncthreads();
+}
+
+// m-tiles (rows per tile tm) of the four groups lane*4 .. lane*4+3 whose row
+// count lies in [lo, hi].
+__device__ inline int lane_tiles(const GemmArgs& a, const int* offs, int tm, int lo, int hi, int (&cnt)[4]) {
+  const int lane = threadIdx.x & (WAVE - 1);
+  int local = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int gg = lane * 4 + i;
+    int c = 0;
+    if (gg < a.n_groups) {
+      const int n = offs[gg + 1] - offs[gg];
+      if (n >= lo && n <= hi) c = ceil_div(n, tm);
+    }
+    cnt[i] = c;
+    local += c;
+  }
+  return local;
+}
+
+// Locate m-tile `tile` among those groups. Wave-uniform; false past the
+// last tile. offs: the staged offsets.
+__device__ inline bool locate_tile_lds(const GemmArgs& a, const int* offs, int tile, int tm, int lo, int hi, int& g,
+                                       int& row0, int& nrows, int& out0) {
   if (a.offsets == nullptr) {
     g = 0;
     row0 = tile * tm;
@@ -19,20 +50,8 @@ __device__ inline bool locate_tile_lds(const GemmArgs& a, int tile, int tm, int 
     return nrows > 0;
   }
   const int lane = threadIdx.x & (WAVE - 1);
-  const int base = a.offsets[a.first];
   int cnt[4];
-  int local = 0;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int gg = lane * 4 + i;
-    int c = 0;
-    if (gg < a.n_groups) {
-      const int n = a.offsets[a.first + gg + 1] - a.offsets[a.first + gg];
-      if (n >= lo && n <= hi) c = ceil_div(n, tm);
-    }
-    cnt[i] = c;
-    local += c;
-  }
+  const int local = lane_tiles(a, offs, tm, lo, hi, cnt);
   int incl = local;
 #pragma unroll
   for (int d = 1; d < WAVE; d <<= 1) {
@@ -60,28 +79,17 @@ __device__ inline bool locate_tile_lds(const GemmArgs& a, int tile, int tm, int 
   }
   g = __shfl(my_g, src, WAVE);
   const int mt = __shfl(my_mt, src, WAVE);
-  const int gbeg = a.offsets[a.first + g];
-  const int gend = a.offsets[a.first + g + 1];
-  row0 = gbeg + mt * tm;
-  nrows = min(tm, gend - row0);
-  out0 = row0 - base;
+  row0 = offs[g] + mt * tm;
+  nrows = min(tm, offs[g + 1] - row0);
+  out0 = row0 - offs[0];
   return true;
 }
 
-// Number of m-tiles (rows per tile tm) among the groups whose row count lies
-// in [lo, hi]; dense: ceil(rows / tm). Wave-uniform.
-__device__ inline int count_tiles_lds(const GemmArgs& a, int tm, int lo, int hi) {
+// Number of m-tiles among those groups; dense: ceil(rows / tm). Wave-uniform.
+__device__ inline int count_tiles_lds(const GemmArgs& a, const int* offs, int tm, int lo, int hi) {
   if (a.offsets == nullptr) return ceil_div(a.dense_rows, tm);
-  const int lane = threadIdx.x & (WAVE - 1);
-  int local = 0;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int gg = lane * 4 + i;
-    if (gg < a.n_groups) {
-      const int n = a.offsets[a.first + gg + 1] - a.offsets[a.first + gg];
-      if (n >= lo && n <= hi) local += ceil_div(n, tm);
-    }
-  }
+  int cnt[4];
+  int local = lane_tiles(a, offs, tm, lo, hi, cnt);
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) local += __shfl_xor(local, o, WAVE);
   return local;

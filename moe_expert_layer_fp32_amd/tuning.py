@@ -76,12 +76,13 @@ class TilingCache:
         return None if e is None else dict(e["limits"])
 
     def tune(self, key: str, run: Callable[[L.MoeTuning | None, int], None], sync: Callable[[], None],
-             candidates=SHARED_CANDIDATES, calls: int = 20, reps: int = 3) -> dict:
+             candidates=SHARED_CANDIDATES, calls: int = 20, reps: int = 3,
+             clock: Callable[[], float] = time.perf_counter) -> dict:
         """Time every candidate and keep the fastest for `key`. run(tuning, i)
         enqueues the i-th layer call with that moe_tuning; sync() waits for the
         device. Each candidate's time is the best over `reps` rounds of
         `calls` calls (the calls are device-bound, so wall time between two
-        synchronisations is device time)."""
+        synchronisations is device time). clock: seconds, monotonic."""
         cands = {label(lim): lim for lim in (limits(*c) for c in candidates)}
         times: dict[str, float] = {}
         for _ in range(reps):
@@ -90,11 +91,11 @@ class TilingCache:
                 for i in range(3):
                     run(t, i)
                 sync()
-                t0 = time.perf_counter()
+                t0 = clock()
                 for i in range(calls):
                     run(t, i)
                 sync()
-                us = (time.perf_counter() - t0) / calls * 1e6
+                us = (clock() - t0) / calls * 1e6
                 times[name] = min(us, times.get(name, math.inf))
         best = min(times, key=times.get)
         self.table[key] = {"limits": dict(cands[best]), "us": {k: round(v, 2) for k, v in times.items()}}

@@ -3,8 +3,6 @@ of the fastest candidate from timed runs, the table's JSON round trip, the
 load bucket and the key. No call reaches a GPU."""
 from __future__ import annotations
 
-import time
-
 import numpy as np
 import pytest
 
@@ -16,22 +14,24 @@ def TU():
 
 
 def test_fastest_candidate_is_kept(TU, tmp_path):
-    # each candidate's calls cost a known time; (128, 128) is the cheapest
+    # each candidate's calls cost a known time on a simulated clock; (128, 128)
+    # is the cheapest
     cost = {(0, 0): 3e-4, (96, 0): 2e-4, (128, 0): 2e-4, (192, 0): 4e-4, (128, 128): 5e-5, (192, 192): 1e-4}
     calls = []
+    now = [0.0]
 
     def run(t, i):
         key = (0, 0) if t is None else (t.shared_ffn1_wgs, t.shared_ffn2_wgs)
         calls.append(key)
-        time.sleep(cost[key])
+        now[0] += cost[key]
 
     cache = TU.TilingCache()
-    best = cache.tune("k", run, lambda: None, calls=4, reps=2)
+    best = cache.tune("k", run, lambda: None, calls=4, reps=2, clock=lambda: now[0])
     assert best == TU.limits(128, 128)
     assert cache.lookup("k") == best
     # every candidate ran (3 warm-up + 4 timed calls per round, 2 rounds)
     assert {c: calls.count(c) for c in cost} == {c: 14 for c in cost}
-    assert set(cache.table["k"]["us"]) == {TU.label(TU.limits(*c)) for c in cost}
+    assert cache.table["k"]["us"] == {TU.label(TU.limits(*c)): round(v * 1e6, 2) for c, v in cost.items()}
     p = tmp_path / "limits.json"
     cache.save(str(p))
     again = TU.TilingCache.load(str(p))
