@@ -51,25 +51,34 @@ __global__ __launch_bounds__(COMB_THREADS) void combine_kernel(CombineArgs a) {
   __shared__ float s_w[COMB_MAX_K];
   __shared__ int s_n;
   __shared__ float s_wid;
-  if (threadIdx.x == 0) {
-    int n = 0;
-    float wid = 0.f;
-    for (int j = 0; j < a.k; ++j) {
-      const int e = a.topk_idx[size_t(t) * a.k + j];
-      const float w = a.topk_w[size_t(t) * a.k + j];
-      if (e >= a.ffn_begin && e < a.ffn_begin + a.n_ffn) {
-        const int p = a.slot_pos[size_t(t) * a.k + j];
-        if (p >= 0) {
-          s_row[n] = p - a.offsets[a.ffn_begin];
-          s_w[n] = w;
-          ++n;
-        }
-      } else if (e >= a.zero_begin && e < a.zero_begin + a.n_zero) {
-        wid += w;
-      }
+  // Lane j of the first wavefront reads selection j (all k at once), the
+  // expert rows are compacted in selection order with a ballot, and the
+  // identity weights are added in selection order.
+  if (threadIdx.x < WAVE) {
+    const int j = threadIdx.x;
+    int e = -1, p = -1;
+    float w = 0.f;
+    if (j < a.k) {
+      e = a.topk_idx[size_t(t) * a.k + j];
+      w = a.topk_w[size_t(t) * a.k + j];
+      p = a.slot_pos[size_t(t) * a.k + j];
     }
-    s_n = n;
-    s_wid = wid;
+    const int base = a.offsets[a.ffn_begin];
+    const bool row = j < a.k && e >= a.ffn_begin && e < a.ffn_begin + a.n_ffn && p >= 0;
+    const bool ident = j < a.k && e >= a.zero_begin && e < a.zero_begin + a.n_zero;
+    const uint64_t rows = __ballot(row);
+    if (row) {
+      const int q = __popcll(rows & ((1ull << j) - 1));
+      s_row[q] = p - base;
+      s_w[q] = w;
+    }
+    const float wz = ident ? w : 0.f;
+    float wid = 0.f;
+    for (int jj = 0; jj < a.k; ++jj) wid += __shfl(wz, jj, WAVE);
+    if (j == 0) {
+      s_n = __popcll(rows);
+      s_wid = wid;
+    }
   }
   __syncthreads();
   const int n = s_n;
