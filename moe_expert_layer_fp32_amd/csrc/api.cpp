@@ -67,6 +67,10 @@ constexpr int PREFILL_T = 1024;
 constexpr int TARGET_WGS = 256;
 constexpr int MAX_DENSE_SPLITS = 32;  // split-K of dense products (partials added in split order)
 constexpr int PERSISTENT_WGS = 512;   // grid cap of the tiled kernel (it loops over tiles)
+// Tile order of dense products with 128-row tiles: panels of DENSE_GROUP_M
+// m-tiles (LdsArgs::group_m). Measured on the prefill shared expert (8192
+// rows, one stream): gate/up 474 -> 457 us, down 296 -> 274 us.
+constexpr int DENSE_GROUP_M = 8;
 
 struct DensePlan {
   bool lds;
@@ -102,6 +106,7 @@ DensePlan plan_dense(int M, int N, int K, GemmElem el, int nacc, int cap = 0) {
   L.max_rows = INT32_MAX;
   L.part_rows = M;
   L.max_wgs = cap > 0 ? std::min(cap, PERSISTENT_WGS) : PERSISTENT_WGS;
+  L.group_m = L.tile_rows >= 128 ? DENSE_GROUP_M : 1;
   p.tiles_y = mt;
   p.partial_bytes = splits > 1 ? size_t(splits) * M * nacc * N * 4 : 0;
   return p;

@@ -329,12 +329,17 @@ __device__ __forceinline__ void gemm_lds_tile(const GemmArgs& a, const LdsArgs& 
 }
 
 // Persistent over tiles: the grid is a fixed number of workgroups (a
-// multiple of 8); the tiles (column block x m-tile, m-tile fastest) are
-// counted on the device from the offsets, cut into 8 contiguous ranges, one
-// per XCD (blocks are dealt to the XCDs round-robin, so block b runs on XCD
-// b % 8), and each workgroup walks its XCD's range with a stride of the
-// workgroups on that XCD. Tiles sharing a weight column block thus run close
-// together in time on one L2.
+// multiple of 8); the tiles (column block x m-tile) are counted on the
+// device from the offsets, cut into 8 contiguous ranges, one per XCD
+// (blocks are dealt to the XCDs round-robin, so block b runs on XCD b % 8),
+// and each workgroup walks its XCD's range with a stride of the workgroups
+// on that XCD. The order is m-tile fastest (group_m <= 1): tiles sharing a
+// weight column block run close together in time on one L2. With
+// group_m > 1 it walks panels of group_m m-tiles, m-tile fastest inside a
+// panel and column block next: the workgroups running together on an XCD
+// then share both the weights of a few column blocks and the activation
+// rows of a few m-tiles in its L2 (the order for dense products with many
+// m-tiles, whose activation rows are re-read once per column block).
 template <class Tr, int S, int EPI, int NF, int BM>
 constexpr int ring_steps() { return S == 1 || BM == 128 ? 8 : 4; }
 template <class Tr, int S, int EPI, int NF, int BM>
@@ -353,9 +358,19 @@ void gemm_lds_kernel(GemmArgs a, LdsArgs L) {
   const int xcd = blockIdx.x % 8, slot = blockIdx.x / 8, per_xcd_wg = nwg / 8;
   const int q = ceil_div(total, 8);
   const int lo = xcd * q, hi = min(total, lo + q);
+  const int gm = max(L.group_m, 1);
   for (int logical = lo + slot; logical < hi; logical += per_xcd_wg) {
-    const int tile = logical % tiles;
-    const int nblock = logical / tiles;
+    int tile, nblock;
+    if (gm == 1) {
+      tile = logical % tiles;
+      nblock = logical / tiles;
+    } else {
+      const int pstart = logical / (gm * nblocks) * gm;   // first m-tile of the panel
+      const int pm = min(gm, tiles - pstart);              // the last panel may be short
+      const int within = logical - pstart * nblocks;
+      nblock = within / pm;
+      tile = pstart + within % pm;
+    }
     int g, row0, nrows, out0;
     if (!locate_tile_lds(a, offs, tile, BM, L.min_rows, L.max_rows, g, row0, nrows, out0)) break;
     g = __builtin_amdgcn_readfirstlane(g);

@@ -88,6 +88,8 @@ struct LdsArgs {
   int max_wgs;         // cap of the persistent grid (workgroups per split)
   int fold_reduce;     // splits > 1: launch no reduce pass; the consumer adds
                        // the partial sums in split order (router -> gate)
+  int group_m;         // tile order: <= 1 m-tile fastest; else panels of
+                       // group_m m-tiles, column block next inside a panel
 };
 hipError_t launch_gemm_lds(const GemmArgs& a, const LdsArgs& L, GemmElem elem, int planes, GemmEpi epi,
                            hipStream_t stream, KernelEvents ev = {});

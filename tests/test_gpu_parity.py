@@ -374,6 +374,27 @@ def test_grouped_ffn_large_tiles(T, skew):
     assert lit_s <= U.TOL["bf16"], f"shared rows error {lit_s}"
 
 
+@pytest.mark.parametrize("T", [4200, 4096])
+def test_grouped_ffn_shared_panel_order(T):
+    """A dense expert with many 128-row tiles and no split reduction, walked
+    in panels of 8 m-tiles: 4200 rows give 33 m-tiles (a ragged last tile
+    and a last panel of one m-tile), 4096 rows 32; gate/up and down both 8
+    column blocks. Checked on every row."""
+    L, DeviceLayer, to_device = _L()
+    cfg = MoEConfig(name="panels", T=T, d=1024, E=8, k=2, gate="softmax", n_ffn=2, inter=64, shared_inter=1024,
+                    dtype="bf16")
+    inp = make_inputs(cfg)
+    lay = DeviceLayer(cfg, inp)
+    U.say(f"[gpu] shared expert panel order T={T} d={cfg.d} I_s={cfg.shared_inter}")
+    shared = lay.grouped_ffn(L.FFN_SHARED)
+    torch.cuda.synchronize()
+    X = np.asarray(O.x_f32(inp), np.float32)
+    want = O.shared_ffn(inp, cfg, X)
+    lit, _ = U.output_errors(U.np_of(shared), want, "f32")
+    U.record(test="grouped_ffn_shared_panel_order", T=T, err_rows_literal=lit)
+    assert lit <= U.TOL["bf16"], f"shared rows error {lit}"
+
+
 # ----------------------------------------------------------------------------
 # whole layer
 # ----------------------------------------------------------------------------
