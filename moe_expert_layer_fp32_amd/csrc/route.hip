@@ -99,9 +99,9 @@ __device__ inline void merge_top2_dpp(float& t1, float& t2) {
 
 // FW wavefronts per workgroup. With split-K partial sums FW > 1: wavefront w
 // adds splits w, w + FW, ... (in that order) for the workgroup's four tokens,
-// the FW sums meet in LDS and are added in wavefront order; every wavefront
-// then runs the same gate on the same tokens (no wavefront leaves before the
-// last barrier) and only the first writes the result.
+// the FW sums meet in LDS and are added in wavefront order; then only the
+// first wavefront runs the gate (the others leave after the fold's barrier,
+// so they do not share its SIMD with copies of the same work).
 // Gate and selection for one token held by a row of 16 lanes (lane r holds
 // experts i*16 + r). u: its logits, bias included. sc_row: the row's LDS
 // scratch for its scores (written and read by this wavefront only). Lane
@@ -282,10 +282,11 @@ __global__ __launch_bounds__(FW * WAVE) void gate_topk_kernel(GateArgs a) {
         if (valid[i]) u[i] += a.bias[i * ROW + r];
     }
   }
+  if (FW > 1 && wave != 0) return;   // no barrier follows
   int sel_e;
   float wv;
   gate_row<PL>(a, u, valid, r, &sc_lds[row][0], sel_e, wv);
-  if (wave == 0 && live && r < a.k) {
+  if (live && r < a.k) {
     a.topk_idx[size_t(t) * a.k + r] = sel_e;
     a.topk_w[size_t(t) * a.k + r] = wv;
   }
