@@ -158,11 +158,7 @@ __device__ __forceinline__ void gate_row(const GateArgs& a, float (&u)[PL], cons
       gs[j] = -INFINITY;
       gc[j] = j * ROW + r < a.n_group;
     }
-    for (int g = 0; g < a.n_group; ++g) {
-      float t1 = -INFINITY, t2 = -INFINITY;
-#pragma unroll
-      for (int i = 0; i < PL; ++i)
-        if (grp[i] == g) merge_top2(t1, t2, sc[i], -INFINITY);
+    auto finish_group = [&](int g, float t1, float t2) {
       merge_top2_dpp<DPP_QUAD_1032>(t1, t2);
       merge_top2_dpp<DPP_QUAD_2301>(t1, t2);
       merge_top2_dpp<DPP_ROW_HALF_MIRROR>(t1, t2);
@@ -170,6 +166,32 @@ __device__ __forceinline__ void gate_row(const GateArgs& a, float (&u)[PL], cons
 #pragma unroll
       for (int j = 0; j < GROUP_SLOTS; ++j)
         if (j * ROW + r == g) gs[j] = t1 + t2;
+    };
+    const int gsize = a.E / a.n_group;
+    const int spg = gsize / ROW;   // slots per group when groups are whole slots
+    if (gsize >= ROW && gsize % ROW == 0 && a.E % ROW == 0) {
+      // Slot i of every lane holds experts i*16 .. i*16+15, all in group
+      // i / spg: one pass over the slots, a group closed after its last slot
+      // (a wave-uniform branch).
+      float t1 = -INFINITY, t2 = -INFINITY;
+#pragma unroll
+      for (int i = 0; i < PL; ++i) {
+        if (i * ROW < a.E) {
+          merge_top2(t1, t2, sc[i], -INFINITY);
+          if ((i + 1) % spg == 0) {
+            finish_group(i / spg, t1, t2);
+            t1 = t2 = -INFINITY;
+          }
+        }
+      }
+    } else {
+      for (int g = 0; g < a.n_group; ++g) {
+        float t1 = -INFINITY, t2 = -INFINITY;
+#pragma unroll
+        for (int i = 0; i < PL; ++i)
+          if (grp[i] == g) merge_top2(t1, t2, sc[i], -INFINITY);
+        finish_group(g, t1, t2);
+      }
     }
     uint32_t gob[GROUP_SLOTS];
 #pragma unroll

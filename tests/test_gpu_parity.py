@@ -127,6 +127,29 @@ def test_route_topk(name, T):
     assert amb.mean() < 0.05
 
 
+@pytest.mark.parametrize("E,n_group,topk_group,k,gate", [
+    (96, 12, 3, 6, "sigmoid"),    # groups of 8 experts: not whole 16-lane slots
+    (64, 4, 2, 4, "softmax"),     # groups of 16: one slot per group
+    (160, 5, 2, 8, "sigmoid"),    # groups of 32 with two unused slots per lane (12 slots launched)
+])
+def test_route_group_limited_shapes(E, n_group, topk_group, k, gate):
+    """Group-limited selection over group sizes that do and do not fill whole
+    16-lane slots (the gate scores groups in one pass over the slots only in
+    the second case)."""
+    L, DeviceLayer, to_device = _L()
+    cfg = MoEConfig(name="groups", T=200, d=256, E=E, k=k, gate=gate, n_group=n_group, topk_group=topk_group,
+                    dtype="bf16")
+    inp = make_inputs(cfg)
+    U.say(f"[gpu] route group-limited E={E} groups={n_group} keep={topk_group} k={k} {gate}")
+    lay = DeviceLayer(cfg, inp)
+    idx, w = lay.route_topk()
+    torch.cuda.synchronize()
+    ref = dict(zip(("z", "scores", "idx", "w"), O.route(inp, cfg)))
+    amb = U.compare_routing(cfg, ref, U.np_of(idx), U.np_of(w), U.x64_of(inp),
+                            inp["w_router"].astype(np.float64))
+    assert amb.mean() < 0.05
+
+
 def test_route_exact_ties_go_to_lower_id():
     """Duplicated router columns give bit-identical logits on both sides; the
     lower expert id must win every such tie."""
