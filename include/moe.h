@@ -213,6 +213,18 @@ typedef struct moe_aux {
     void* ev_fork;
     void* ev_join;
     const moe_tuning* tuning; /* launch limits (see moe_tuning), or NULL */
+    /* Optional copies of the routed-expert intermediates: when given, the
+     * layer writes them there instead of into its workspace. Rows are the
+     * slots of resident FFN experts in expert order (offsets[ffn_begin]
+     * onwards), compact, at most T*k of them; only the first
+     * R = offsets[ffn_begin + n_ffn] - offsets[ffn_begin] are written.
+     * Ignored when the layer has no resident FFN expert. */
+    void* h;              /* [T*k][inter] SwiGLU output h = silu(x W1) * (x W3):
+                           * float for F32 and W8A8, bf16 for BF16 */
+    int8_t* q_h;          /* W8A8: [T*k][inter] int8 codes of h */
+    float* s_h;           /* W8A8: [T*k] their per-row scales */
+    void* rows;           /* [T*k][d] expert output rows h W2 before the gate
+                           * weights: float for F32 and W8A8, bf16 for BF16 */
 } moe_aux;
 
 /* Workspace bytes an entry point needs for this descriptor (0 if none). */

@@ -732,6 +732,12 @@ moe_status moe_layer(const moe_desc* d, const moe_weights* w, const void* x, voi
   auto routed_caps = [&](const FfnPlan& p) { return with_caps(p, tune.routed_ffn1_wgs, tune.routed_ffn2_wgs); };
   if (A.q_x) L.routed.qx = L.shared.qx = A.q_x;
   if (A.s_x) L.routed.sx = L.shared.sx = A.s_x;
+  if (d->n_ffn > 0) {
+    if (A.h) L.routed.h = static_cast<uint8_t*>(A.h);
+    if (A.q_h && w8a8(d)) L.routed.qh = A.q_h;
+    if (A.s_h && w8a8(d)) L.routed.sh = A.s_h;
+    if (A.rows) L.rows = A.rows;
+  }
 
   // The shared expert needs only x (and its int8 codes): it is forked onto
   // the caller's second stream, when one is given, before routing starts.

@@ -159,8 +159,11 @@ class DeviceLayer:
         return y
 
     def layer_with_tables(self, x=None, ws=None, second: SecondStream | None = None,
-                          tuning: L.MoeTuning | None = None):
-        """moe_layer plus its routing tables (and W8A8 activation codes) via moe_aux."""
+                          tuning: L.MoeTuning | None = None, intermediates: bool = False):
+        """moe_layer plus its routing tables (and W8A8 activation codes) via
+        moe_aux; with `intermediates`, also the routed SwiGLU rows h, the expert
+        output rows and (W8A8) the int8 codes and scales of h, T*k rows of
+        capacity each."""
         x = self.x if x is None else x
         T, k, E, dev = x.shape[0], self.cfg.k, self.cfg.E, self.device
         t = dict(topk_idx=torch.empty((T, k), dtype=torch.int32, device=dev),
@@ -172,6 +175,14 @@ class DeviceLayer:
         if self.cfg.dtype == "w8a8":
             t["q_x"] = torch.empty((T, self.cfg.d), dtype=torch.int8, device=dev)
             t["s_x"] = torch.empty(T, dtype=torch.float32, device=dev)
+        if intermediates and self.cfg.n_ffn > 0:
+            cap = max(T * k, 1)
+            fdt = torch.bfloat16 if self.cfg.dtype == "bf16" else torch.float32
+            t["h"] = torch.empty((cap, self.cfg.inter), dtype=fdt, device=dev)
+            t["rows"] = torch.empty((cap, self.cfg.d), dtype=fdt, device=dev)
+            if self.cfg.dtype == "w8a8":
+                t["q_h"] = torch.empty((cap, self.cfg.inter), dtype=torch.int8, device=dev)
+                t["s_h"] = torch.empty(cap, dtype=torch.float32, device=dev)
         aux = L.MoeAux(**{n: L.ptr(v) for n, v in t.items()})
         y = self.layer(x, aux=aux, ws=ws, second=second, tuning=tuning)
         return y, t

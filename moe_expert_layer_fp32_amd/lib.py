@@ -62,7 +62,8 @@ class MoeAux(ctypes.Structure):
     _fields_ = [("topk_idx", _vp), ("topk_w", _vp), ("counts", _vp), ("offsets", _vp), ("sorted_slot", _vp),
                 ("slot_pos", _vp), ("q_x", _vp), ("s_x", _vp), ("ev_ffn1_begin", _vp), ("ev_ffn1_end", _vp),
                 ("ev_ffn2_begin", _vp), ("ev_ffn2_end", _vp), ("stream2", _vp), ("ev_fork", _vp),
-                ("ev_join", _vp), ("tuning", ctypes.POINTER(MoeTuning))]
+                ("ev_join", _vp), ("tuning", ctypes.POINTER(MoeTuning)), ("h", _vp), ("q_h", _vp), ("s_h", _vp),
+                ("rows", _vp)]
 
 
 _lib_handle = None

@@ -477,6 +477,97 @@ def test_layer_prefill_sampled_tokens():
     _check_layer(cfg, inp, lay, tokens=np.sort(toks))
 
 
+def _f32(v):
+    return np.asarray(v, dtype=np.float32)
+
+
+def _check_w8a8_integer_products(cfg, inp, t, silu_exact):
+    """The W8A8 layer's integer products through its own intermediates:
+    - h codes and scales: bit-exact against quantising the GPU's own h;
+    - down projection: every expert output row bit-exact against the exact
+      integer product of the GPU's own h codes with the int8 weights, scaled
+      as the kernel scales its int32 accumulator (float(acc) * s_h * s_w2,
+      each product rounded to fp32);
+    - gate/up (silu_exact): h bit-exact against the exact integer products of
+      the int8 x codes, scaled the same way, when every gate value is large
+      enough (>= 20) that the kernel's SiLU returns its argument exactly;
+      else within a few fp32 ulps of SiLU of those scaled products.
+    A one-step error in an int32 accumulator below 2^24 changes the fp32
+    value it is converted to, and with it these results."""
+    offsets, ss = U.np_of(t["offsets"]), U.np_of(t["sorted_slot"])
+    qx, sx = U.np_of(t["q_x"]), U.np_of(t["s_x"])
+    q_ref, s_ref = O.quantise_rows(np.asarray(O.x_f32(inp), np.float32))
+    assert np.array_equal(qx, q_ref) and np.array_equal(sx.view(np.uint32), s_ref.view(np.uint32))
+    h, qh, sh, rows = (U.np_of(t[n]) for n in ("h", "q_h", "s_h", "rows"))
+    base = offsets[cfg.ffn_begin]
+    max_acc = 0
+    for el in range(cfg.n_ffn):
+        e = cfg.ffn_begin + el
+        r0, r1 = offsets[e] - base, offsets[e + 1] - base
+        if r1 == r0:
+            continue
+        tok = ss[offsets[e]:offsets[e + 1]] // cfg.k
+        A = O.int_matmul(qx[tok], inp["w1"][el])
+        B = O.int_matmul(qx[tok], inp["w3"][el])
+        ga = _f32(_f32(_f32(A) * sx[tok][:, None]) * _f32(inp["s1"][el])[None, :])
+        up = _f32(_f32(_f32(B) * sx[tok][:, None]) * _f32(inp["s3"][el])[None, :])
+        hg = h[r0:r1]
+        if silu_exact:
+            assert ga.min() >= 20.0, "precondition of the exact SiLU"
+            assert np.array_equal(hg.view(np.uint32), _f32(ga * up).view(np.uint32)), f"h of expert {e}"
+        else:
+            want = O.silu(ga.astype(np.float64)) * up.astype(np.float64)
+            tol = 8 * 2.0 ** -23 * np.abs(want) + 1e-6 * np.abs(want).max()
+            assert np.all(np.abs(hg - want) <= tol), f"h of expert {e}"
+        q_own, s_own = O.quantise_rows(hg)
+        assert np.array_equal(qh[r0:r1], q_own) and np.array_equal(sh[r0:r1].view(np.uint32), s_own.view(np.uint32))
+        Y = O.int_matmul(qh[r0:r1], inp["w2"][el])
+        max_acc = max(max_acc, float(np.abs(Y).max()), float(np.abs(A).max()), float(np.abs(B).max()))
+        want_rows = _f32(_f32(_f32(Y) * sh[r0:r1][:, None]) * _f32(inp["s2"][el])[None, :])
+        assert np.array_equal(rows[r0:r1].view(np.uint32), want_rows.view(np.uint32)), f"rows of expert {e}"
+    return max_acc
+
+
+def test_w8a8_integer_products_full_layer():
+    """The W8A8 workload (T 456, d 5120, 64 experts) through moe_layer's own
+    intermediates: down projection and h codes bit-exact, gate/up within the
+    SiLU's few ulps of the exact integer products."""
+    cfg, inp = U.inputs("pangu_moge_w8a8")
+    lay = U.device_layer("pangu_moge_w8a8")
+    U.say("[gpu] W8A8 integer products pangu_moge_w8a8 (full layer)")
+    _, t = lay.layer_with_tables(intermediates=True)
+    torch.cuda.synchronize()
+    max_acc = _check_w8a8_integer_products(cfg, inp, t, silu_exact=False)
+    U.record(test="w8a8_integer_products_full_layer", max_abs_accumulator=max_acc)
+
+
+@pytest.mark.parametrize("T,E,k,inter", [(64, 8, 2, 256), (300, 64, 4, 512)])
+def test_w8a8_integer_products_exact(T, E, k, inter):
+    """Bit-exact int32 accumulators of both W8A8 products: non-negative x and
+    gate weights, gate scales raised so every gate value is >= 20, where the
+    kernel's SiLU is exactly its argument. 8 experts of inter 256 split the
+    gate/up reduction over two workgroups per tile (partial sums added by the
+    reduce pass); 64 experts of inter 512 run unsplit."""
+    L, DeviceLayer, to_device = _L()
+    cfg = MoEConfig(name="w8exact", T=T, d=1024, E=E, k=k, gate="softmax", n_ffn=E, inter=inter, dtype="w8a8")
+    inp = make_inputs(cfg, seed=3)
+    inp["x"] = inp["x"] & np.uint16(0x7FFF)                 # bf16 bits: clear the sign
+    inp["w1"] = np.abs(inp["w1"]).astype(np.int8)
+    qx, sx = O.quantise_rows(np.asarray(O.x_f32(inp), np.float32))
+    for el in range(cfg.n_ffn):
+        A = O.int_matmul(qx, inp["w1"][el])
+        a_min = (A * sx[:, None].astype(np.float64) * inp["s1"][el][None, :].astype(np.float64)).min()
+        if a_min < 24.0:
+            inp["s1"][el] = (inp["s1"][el] * np.float32(24.0 / max(a_min, 1e-3))).astype(np.float32)
+    lay = DeviceLayer(cfg, inp)
+    U.say(f"[gpu] W8A8 integer products exact T={T} E={E} inter={inter}")
+    _, t = lay.layer_with_tables(intermediates=True)
+    torch.cuda.synchronize()
+    max_acc = _check_w8a8_integer_products(cfg, inp, t, silu_exact=True)
+    assert max_acc < 2 ** 24
+    U.record(test="w8a8_integer_products_exact", T=T, max_abs_accumulator=max_acc)
+
+
 def _bits(t):
     return t.view(torch.int16) if t.dtype == torch.bfloat16 else t
 
