@@ -130,6 +130,29 @@ def ffn1_algorithmic(cfg, counts_per_layer):
     return out
 
 
+def layer_algorithmic(cfg, counts_per_layer):
+    """Algorithmic work of one whole layer call (the survey's count):
+    bytes = W1, W3 and W2 (and int8 scales) of every resident FFN expert that
+    received tokens, the shared expert's weights, the fp32 router (4 d E) and
+    x read plus y written (T d each, in the layer's element type); flops =
+    the expert and shared-expert products, 2 n_e 3 d I per expert and
+    2 T 3 d I_s (the router's 2 T d E is counted apart)."""
+    wb = {"f32": 4, "bf16": 2, "w8a8": 1}[cfg.dtype]
+    xb = {"f32": 4, "bf16": 2, "w8a8": 2}[cfg.dtype]
+    scale_b = 4 if cfg.dtype == "w8a8" else 0
+    shared_b = 3 * cfg.d * cfg.shared_inter * wb + (2 * cfg.shared_inter + cfg.d) * scale_b if cfg.shared_inter else 0
+    out = []
+    for counts in counts_per_layer:
+        res = counts[cfg.ffn_begin:cfg.ffn_begin + cfg.n_ffn]
+        active = int((res > 0).sum())
+        R = int(res.sum())
+        byts = (active * (3 * cfg.d * cfg.inter * wb + (2 * cfg.inter + cfg.d) * scale_b) + shared_b
+                + 4 * cfg.d * cfg.E + 2 * cfg.T * cfg.d * xb)
+        flops = 2.0 * R * 3 * cfg.d * cfg.inter + 2.0 * cfg.T * 3 * cfg.d * cfg.shared_inter
+        out.append((byts, flops))
+    return out
+
+
 def cpu_baseline(cfg, inp, seconds: float):
     """The oracle as it stands, timed on this host on a bounded sample."""
     import numpy as np
@@ -303,6 +326,20 @@ def main() -> int:
         if tr.get("kernel_sha") == kernel_hash() and tr.get("workload") == cfg.name:
             roof["traffic"] = tr.get("bytes_per_launch")
 
+    # The whole layer call against the same roofline: algorithmic bytes (or
+    # flops) per call over the measured time per call.
+    lay_alg = layer_algorithmic(cfg, counts_per_layer)
+    step_s = wall / K
+    if prefill:
+        la = float(np.mean([lay_alg[i % n_layers][1] for i in range(K)])) / step_s / 1e12
+        layer_roof = {"bound": "mfma", "achieved": round(la, 2), "peak": roof["peak"], "unit": "TFLOP/s"}
+    else:
+        la = float(np.mean([lay_alg[i % n_layers][0] for i in range(K)])) / step_s / 1e9
+        layer_roof = {"bound": "hbm", "achieved": round(la, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s"}
+    layer_roof["frac"] = round(layer_roof["achieved"] / layer_roof["peak"], 4)
+    layer_roof["alg_per_call"] = (float(np.mean([a[1] for a in lay_alg])) if prefill
+                                  else int(np.mean([a[0] for a in lay_alg])))
+
     graph = None
     if args.graph:
         graph = graph_replay(L, layers, desc, y, ws, second, K, t_struct if tuned else None)
@@ -330,6 +367,7 @@ def main() -> int:
                    "streams": 2 if second is not None else 1,
                    "global_batch": cfg.T, "parallelism": "none (1 GPU)"},
         "roofline": roof,
+        "layer_roofline": layer_roof,
         "cpu_baseline": cpu,
     }
     if tuned is not None:
