@@ -1,0 +1,70 @@
+"""Host-side checks of bench.py's algorithmic work counts (no GPU).
+
+The whole-layer byte count is pinned to the sizes worked out by hand from
+the workload shapes (every resident expert active): weights of the resident
+experts and of the shared expert, the fp32 router, x read and y written."""
+from __future__ import annotations
+
+import importlib.util
+import os
+
+import numpy as np
+import pytest
+
+from moe_inputs import get
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _bench():
+    spec = importlib.util.spec_from_file_location("bench_under_test", os.path.join(ROOT, "bench.py"))
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    return mod
+
+
+def _all_active(cfg, rows_each=3):
+    c = np.zeros(cfg.E, np.int64)
+    c[cfg.ffn_begin:cfg.ffn_begin + cfg.n_ffn] = rows_each
+    return c
+
+
+# (workload, bytes per call with every resident expert active), written out
+# from the shapes: n_ffn * 3 d I * w (+ int8 scales 4 (2I + d) per expert),
+# shared 3 d I_s * w (+ scales), router 4 d E, x and y 2 * T d * xb.
+HAND = {
+    "longcat_zero_bf16": 64 * 3 * 1024 * 512 * 2 + 4 * 1024 * 96 + 2 * 256 * 1024 * 2,
+    "dsv3_decode_share_bf16": 8 * 3 * 7168 * 2048 * 2 + 3 * 7168 * 2048 * 2 + 4 * 7168 * 256 + 2 * 512 * 7168 * 2,
+    "pangu_moge_w8a8": (64 * (3 * 5120 * 1536 + 4 * (2 * 1536 + 5120)) + 3 * 5120 * 4096 + 4 * (2 * 4096 + 5120)
+                        + 4 * 5120 * 64 + 2 * 456 * 5120 * 2),
+    "prefill_zipf_bf16": 32 * 3 * 7168 * 2048 * 2 + 3 * 7168 * 2048 * 2 + 4 * 7168 * 256 + 2 * 8192 * 7168 * 2,
+}
+
+
+@pytest.mark.parametrize("name", sorted(HAND))
+def test_layer_bytes_match_hand_count(name):
+    B = _bench()
+    cfg = get(name)
+    (byts, flops), = B.layer_algorithmic(cfg, [_all_active(cfg)])
+    assert byts == HAND[name]
+    R = 3 * cfg.n_ffn
+    assert flops == 2.0 * R * 3 * cfg.d * cfg.inter + 2.0 * cfg.T * 3 * cfg.d * cfg.shared_inter
+
+
+def test_layer_bytes_count_only_experts_with_tokens():
+    B = _bench()
+    cfg = get("dsv3_decode_share_bf16")
+    c = _all_active(cfg)
+    c[cfg.ffn_begin + 2] = 0
+    (full, _), (fewer, _) = B.layer_algorithmic(cfg, [_all_active(cfg), c])
+    assert full - fewer == 3 * cfg.d * cfg.inter * 2
+
+
+def test_gate_up_bytes_and_flops():
+    B = _bench()
+    cfg = get("longcat_zero_bf16")
+    c = _all_active(cfg, rows_each=5)
+    (byts, flops, R, active), = B.ffn1_algorithmic(cfg, [c])
+    assert (R, active) == (5 * 64, 64)
+    assert byts == 64 * 2 * 1024 * 512 * 2 + R * 1024 * 2 + R * 512 * 2
+    assert flops == 2.0 * R * 1024 * 2 * 512
