@@ -203,6 +203,9 @@ typedef struct moe_aux {
      * DeepSeek-V3/R1-on-Ascend page (Huxiu), section 模型侧并发优化, item
      * 计算通信并发, and the two-stream overlap on page "LongCat-Flash与
      * GLM-4.6V ...", section 破局之道：多流并行与Single-Batch Overlap.
+     * For W8A8 the int8 codes of x are computed on stream2 too, ahead of
+     * the shared expert and beside the router; the routed products on
+     * `stream` wait for them through ev_join, which is recorded twice.
      * stream2 must be a non-NULL stream of the same device other than
      * `stream`; the events are hipEvent_t created by the caller. Giving only
      * some of the three, or stream2 equal to `stream`, is

@@ -742,18 +742,27 @@ moe_status moe_layer(const moe_desc* d, const moe_weights* w, const void* x, voi
   // The shared expert needs only x (and its int8 codes): it is forked onto
   // the caller's second stream, when one is given, before routing starts.
   const bool fork = d->T > 0 && d->shared_inter > 0 && A.stream2 && A.ev_fork && A.ev_join;
-  if (d->T > 0 && w8a8(d)) {
-    st = run_quant_x(d, x, L.routed, s);
-    if (st != MOE_OK) return st;
-  }
+  const bool quant = d->T > 0 && w8a8(d);
+  hipStream_t s2 = static_cast<hipStream_t>(A.stream2);
+  hipEvent_t ev_join = static_cast<hipEvent_t>(A.ev_join);
   if (fork) {
-    hipStream_t s2 = static_cast<hipStream_t>(A.stream2);
     HIP_TRY(hipEventRecord(static_cast<hipEvent_t>(A.ev_fork), s));
     HIP_TRY(hipStreamWaitEvent(s2, static_cast<hipEvent_t>(A.ev_fork), 0));
+    if (quant) {
+      // The int8 codes of x on the second stream, ahead of the shared expert
+      // and beside the router (which reads x itself); the routed products
+      // wait for this record of ev_join, which is recorded again after the
+      // shared expert (a wait takes the record made before it).
+      st = run_quant_x(d, x, L.routed, s2);
+      if (st != MOE_OK) return st;
+      HIP_TRY(hipEventRecord(ev_join, s2));
+    }
     st = run_ffn(d, shared_caps(shared_plan(d, w)), x, L.shared, L.shared_rows, rb, s2, nullptr, nullptr, nullptr,
                  nullptr);
     if (st != MOE_OK) return st;
-    HIP_TRY(hipEventRecord(static_cast<hipEvent_t>(A.ev_join), s2));
+  } else if (quant) {
+    st = run_quant_x(d, x, L.routed, s);
+    if (st != MOE_OK) return st;
   }
   if (d->T > 0) {
     st = run_route(d, w, x, idx, tw, L.route, s);
@@ -762,13 +771,15 @@ moe_status moe_layer(const moe_desc* d, const moe_weights* w, const void* x, voi
   HIP_TRY(launch_permute(idx, d->T * d->k, d->E, counts, offsets, sorted_slot, slot_pos, L.chunk_hist, s));
   if (d->T == 0) return MOE_OK;
   if (d->n_ffn > 0) {
+    if (fork && quant) HIP_TRY(hipStreamWaitEvent(s, ev_join, 0));   // the codes of x
     st = run_ffn(d, routed_caps(routed_plan(d, w, offsets, sorted_slot)), x, L.routed, L.rows, rb, s,
                  static_cast<hipEvent_t>(A.ev_ffn1_begin), static_cast<hipEvent_t>(A.ev_ffn1_end),
                  static_cast<hipEvent_t>(A.ev_ffn2_begin), static_cast<hipEvent_t>(A.ev_ffn2_end));
     if (st != MOE_OK) return st;
   }
   if (fork) {
-    HIP_TRY(hipStreamWaitEvent(s, static_cast<hipEvent_t>(A.ev_join), 0));
+    HIP_TRY(hipEventRecord(ev_join, s2));   // after the shared expert on stream2
+    HIP_TRY(hipStreamWaitEvent(s, ev_join, 0));
   } else if (d->shared_inter > 0) {
     st = run_ffn(d, shared_caps(shared_plan(d, w)), x, L.shared, L.shared_rows, rb, s, nullptr, nullptr, nullptr,
                  nullptr);
