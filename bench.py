@@ -319,6 +319,7 @@ def main() -> int:
     roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
     roof["kernel"] = "routed-expert gate/up projection + SwiGLU (one launch per step)"
     roof["mean_us"] = round(mean_s * 1e6, 2)
+    roof["p10_p50_p90_us"] = [round(float(v) * 1e3, 2) for v in np.percentile(ffn1_ms, [10, 50, 90])]
     roof["alg_bytes_per_launch"] = int(alg_bytes.mean())
     roof["traffic"] = None
     if os.path.exists(TRAFFIC_FILE):
