@@ -312,6 +312,77 @@ def test_grouped_ffn_routed(name, T, skew):
     assert beyond_flips <= U.TOL[cfg.dtype], f"rows error {beyond_flips} (literal {lit})"
 
 
+# rows per resident expert at the tile boundaries: none, one, 63/64/65
+# (one 64-row tile, or the switch from the 64-row to the 128-row launch at
+# prefill sizes), 127/128/129 (one or two 128-row tiles, two or three 64-row)
+BOUNDARY_COUNTS = (0, 1, 63, 64, 65, 127, 128, 129)
+
+
+@pytest.mark.parametrize("T", [600, 1100])
+@pytest.mark.parametrize("dtype", ["bf16", "w8a8"])
+def test_grouped_ffn_tile_boundaries(T, dtype):
+    """Resident experts with exactly 0, 1, 63, 64, 65, 127, 128 and 129 rows,
+    in the decode regime (600 tokens: 64-row tiles) and the prefill regime
+    (1100 tokens: 64-row launch up to 64 rows, 128-row launch above); the
+    other tokens go to non-resident experts. Every row against the oracle."""
+    L, DeviceLayer, to_device = _L()
+    cfg = MoEConfig(name="bounds", T=T, d=256, E=16, k=1, gate="softmax", n_ffn=8, inter=128, dtype=dtype)
+    inp = make_inputs(cfg, seed=7)
+    lay = DeviceLayer(cfg, inp)
+    g = np.random.default_rng(19)
+    ids = np.concatenate([np.full(c, e, np.int32) for e, c in enumerate(BOUNDARY_COUNTS)])
+    rest = g.integers(8, 16, size=T - ids.size).astype(np.int32)
+    idx = g.permutation(np.concatenate([ids, rest])).reshape(T, 1).astype(np.int32)
+    U.say(f"[gpu] tile boundaries T={T} {dtype} counts={BOUNDARY_COUNTS}")
+    counts, offsets, ss, sp = lay.permute(torch.from_numpy(idx).cuda())
+    rows = lay.grouped_ffn(L.FFN_ROUTED, offsets, ss)
+    torch.cuda.synchronize()
+    assert U.np_of(counts)[:8].tolist() == list(BOUNDARY_COUNTS)
+    want, allow = _expected_rows(cfg, inp, idx, O.routing_tables(idx, cfg.E))
+    got = U.np_of(rows)[: want.shape[0]]
+    rms = float(np.sqrt(np.mean(want ** 2)))
+    beyond_flips = float(np.maximum(np.abs(got - want) - allow, 0).max() / rms)
+    U.record(test="grouped_ffn_tile_boundaries", T=T, dtype=dtype, err_rows_beyond_code_flips=beyond_flips)
+    assert beyond_flips <= U.TOL[dtype], f"rows error {beyond_flips}"
+
+
+@pytest.mark.parametrize("name", ["longcat_zero_bf16", "pangu_moge_w8a8"])
+def test_layer_writes_nothing_outside_its_buffers(name):
+    """Guard bands around y and every moe_aux output buffer (filled with a
+    fixed byte pattern) are untouched after a layer call, and the routed rows
+    and h buffers are not written past the R rows the routing produced."""
+    L, DeviceLayer, to_device = _L()
+    cfg, inp = U.inputs(name)
+    lay = U.device_layer(name)
+    U.say(f"[gpu] guard bands {name}")
+    T, k, E, d = cfg.T, cfg.k, cfg.E, cfg.d
+    G = 4096                      # guard bytes on each side
+    PAT = 0x5A
+
+    def guarded(nbytes):
+        buf = torch.full((nbytes + 2 * G,), PAT, dtype=torch.uint8, device="cuda")
+        return buf, buf[G:G + nbytes]
+
+    shapes = dict(topk_idx=T * k * 4, topk_w=T * k * 4, counts=E * 4, offsets=(E + 1) * 4, sorted_slot=T * k * 4,
+                  slot_pos=T * k * 4, h=T * k * cfg.inter * (2 if cfg.dtype == "bf16" else 4),
+                  rows=T * k * d * (2 if cfg.dtype == "bf16" else 4))
+    if cfg.dtype == "w8a8":
+        shapes.update(q_x=T * d, s_x=T * 4, q_h=T * k * cfg.inter, s_h=T * k * 4)
+    bufs = {n: guarded(b) for n, b in shapes.items()}
+    ybuf, yv = guarded(T * d * 2)
+    aux = L.MoeAux(**{n: L.ptr(v) for n, (_, v) in bufs.items()})
+    lay.layer(y=yv.view(torch.bfloat16).view(T, d), aux=aux)
+    torch.cuda.synchronize()
+    for n, (buf, _) in list(bufs.items()) + [("y", (ybuf, yv))]:
+        b = U.np_of(buf)
+        assert (b[:G] == PAT).all() and (b[-G:] == PAT).all(), f"{n} written outside its buffer"
+    offs = U.np_of(bufs["offsets"][1].view(torch.int32))
+    R = int(offs[cfg.ffn_begin + cfg.n_ffn] - offs[cfg.ffn_begin])
+    for n, width in (("rows", d * (2 if cfg.dtype == "bf16" else 4)), ("h", cfg.inter * (2 if cfg.dtype == "bf16" else 4))):
+        tail = U.np_of(bufs[n][1])[R * width:]
+        assert (tail == PAT).all(), f"{n} written past row {R}"
+
+
 @pytest.mark.parametrize("name", ["dsv3_decode_share_bf16", "pangu_moge_w8a8"])
 def test_grouped_ffn_shared(name):
     L, DeviceLayer, to_device = _L()
