@@ -68,3 +68,14 @@ def test_gate_up_bytes_and_flops():
     assert (R, active) == (5 * 64, 64)
     assert byts == 64 * 2 * 1024 * 512 * 2 + R * 1024 * 2 + R * 512 * 2
     assert flops == 2.0 * R * 1024 * 2 * 512
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """One GPU only: --gpus 2 exits with status 2 and says why, before any
+    device work."""
+    import subprocess
+    import sys
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
