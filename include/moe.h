@@ -194,7 +194,11 @@ typedef struct moe_aux {
     void* ev_ffn1_begin;  /* start / end of the routed-expert gate/up      */
     void* ev_ffn1_end;    /*   projection + SwiGLU (first to last kernel)  */
     void* ev_ffn2_begin;  /* start / end of the routed-expert down         */
-    void* ev_ffn2_end;    /*   projection (first to last kernel)           */
+    void* ev_ffn2_end;    /*   projection (first to last kernel; with a
+                           *   second stream from 1024 tokens up, bf16 and
+                           *   fp32: the down product of the experts with
+                           *   more than 64 rows, the others' running on
+                           *   stream2) */
     /* Shared-expert concurrency: when all three are given (and the layer has
      * a shared expert), the shared FFN runs on stream2, forked from `stream`
      * as soon as its inputs are ready and joined before the combine, so it
@@ -203,6 +207,9 @@ typedef struct moe_aux {
      * DeepSeek-V3/R1-on-Ascend page (Huxiu), section 模型侧并发优化, item
      * 计算通信并发, and the two-stream overlap on page "LongCat-Flash与
      * GLM-4.6V ...", section 破局之道：多流并行与Single-Batch Overlap.
+     * From 1024 tokens up (bf16, fp32) the down product of the experts
+     * with at most 64 rows also runs on stream2, after the shared expert;
+     * ev_fork is recorded a second time for it, after their gate/up.
      * For W8A8 the int8 codes of x are computed on stream2 too, ahead of
      * the shared expert and beside the router; the routed products on
      * `stream` wait for them through ev_join, which is recorded twice.

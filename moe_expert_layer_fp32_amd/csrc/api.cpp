@@ -303,8 +303,22 @@ moe_status run_dense(GemmArgs g, int M, GemmElem el, int planes, GemmEpi epi, vo
 // cap > 0: at most that many workgroups in all (split-K slices included).
 int capped_wgs(int cap, int splits) { return cap > 0 ? std::min(PERSISTENT_WGS, std::max(1, cap / splits)) : PERSISTENT_WGS; }
 
+// Which experts a routed product covers. From PREFILL_T tokens up the two
+// launches (experts with at most 64 rows, experts with more) can be issued
+// apart, on different streams; below, only PART_ALL exists.
+enum RoutedPart { PART_NONE = 0, PART_SMALL = 1, PART_LARGE = 2, PART_ALL = 3 };
+
+// Whether moe_layer may place the two prefill launches of a routed product on
+// different streams: bf16 / fp32 (the W8A8 row quantisation between the
+// products covers every expert at once) and both products tiled unsplit.
+bool routed_parts_apart(const moe_desc* d) {
+  return d->T >= PREFILL_T && !w8a8(d) && d->n_ffn > 0 && routed_tiled(d, d->inter, d->d) &&
+         routed_tiled(d, d->d, d->inter);
+}
+
 moe_status run_routed(GemmArgs g, const moe_desc* d, GemmElem el, int planes, GemmEpi epi, void* partial,
-                      hipStream_t s, KernelEvents ev = {}, int cap = 0) {
+                      hipStream_t s, KernelEvents ev = {}, int cap = 0, int part = PART_ALL) {
+  if (part == PART_NONE) return MOE_OK;
   const int splits = routed_splits(d, g.N, g.K);
   if (splits > 1) {
     LdsArgs L{};
@@ -336,7 +350,10 @@ moe_status run_routed(GemmArgs g, const moe_desc* d, GemmElem el, int planes, Ge
       HIP_TRY(launch_gemm_lds(g, L, el, planes, epi, s, ev));
       return MOE_OK;
     }
-    HIP_TRY(launch_gemm_lds(g, L, el, planes, epi, s, KernelEvents{ev.start, nullptr}));
+    if (part & PART_SMALL)
+      HIP_TRY(launch_gemm_lds(g, L, el, planes, epi, s,
+                              part == PART_SMALL ? ev : KernelEvents{ev.start, nullptr}));
+    if (!(part & PART_LARGE)) return MOE_OK;
     // experts with more rows: 128-row tiles, 64 features per wavefront for
     // one-plane products (twice the matrix-core work per weight fragment)
     L.tile_rows = 128;
@@ -344,7 +361,8 @@ moe_status run_routed(GemmArgs g, const moe_desc* d, GemmElem el, int planes, Ge
     L.max_rows = INT32_MAX;
     L.wave_features = planes == 1 && g.N % 256 == 0 ? 64 : 32;
     g.tiles_y = ceil_div(r_max(d), L.tile_rows) + g.n_groups;
-    HIP_TRY(launch_gemm_lds(g, L, el, planes, epi, s, KernelEvents{nullptr, ev.stop}));
+    HIP_TRY(launch_gemm_lds(g, L, el, planes, epi, s,
+                            part == PART_LARGE ? ev : KernelEvents{nullptr, ev.stop}));
     return MOE_OK;
   }
   g.max_group_rows = 0;
@@ -439,12 +457,19 @@ FfnPlan with_caps(FfnPlan p, int cap1, int cap2) {
   return p;
 }
 
+// part1 / part2: which experts the gate/up and the down product cover
+// (routed products from PREFILL_T tokens up; PART_NONE skips the product).
 moe_status run_ffn(const moe_desc* d, const FfnPlan& p, const void* x, const FfnWs& f, void* rows, bool rows_bf16,
-                   hipStream_t s, hipEvent_t e1b, hipEvent_t e1e, hipEvent_t e2b, hipEvent_t e2e) {
+                   hipStream_t s, hipEvent_t e1b, hipEvent_t e1e, hipEvent_t e2b, hipEvent_t e2e,
+                   int part1 = PART_ALL, int part2 = PART_ALL) {
   const GemmElem el = weight_elem(d);
   const int FB = frag_bytes_of(el);
   const int KF = weight_kf(d);
   const bool routed = p.offsets != nullptr;
+  if (w8a8(d) && (part1 != PART_ALL || part2 != PART_ALL)) return MOE_ERR_UNSUPPORTED;
+  // a dense (shared) product is whole or skipped
+  if (!routed && ((part1 != PART_ALL && part1 != PART_NONE) || (part2 != PART_ALL && part2 != PART_NONE)))
+    return MOE_ERR_UNSUPPORTED;
   moe_status st;
 
   GemmArgs g1{};
@@ -468,9 +493,11 @@ moe_status run_ffn(const moe_desc* d, const FfnPlan& p, const void* x, const Ffn
   g1.ldo = size_t(p.inter) * h_bytes(d);
   g1.out_bf16 = d->dtype == MOE_DTYPE_BF16;
   const KernelEvents ev1{e1b, e1e}, ev2{e2b, e2e};
-  st = routed ? run_routed(g1, d, el, 2, EPI_SWIGLU, f.partial, s, ev1, p.cap1)
-              : run_dense(g1, d->T, el, 2, EPI_SWIGLU, f.partial, s, ev1, p.cap1);
-  if (st != MOE_OK) return st;
+  if (part1 != PART_NONE) {
+    st = routed ? run_routed(g1, d, el, 2, EPI_SWIGLU, f.partial, s, ev1, p.cap1, part1)
+                : run_dense(g1, d->T, el, 2, EPI_SWIGLU, f.partial, s, ev1, p.cap1);
+    if (st != MOE_OK) return st;
+  }
 
   if (w8a8(d)) {
     HIP_TRY(launch_quant_rows(f.h, 0, p.inter, p.rows_bound, p.offsets, p.first, p.groups, f.qh, f.sh, s));
@@ -494,9 +521,11 @@ moe_status run_ffn(const moe_desc* d, const FfnPlan& p, const void* x, const Ffn
   g2.out = static_cast<uint8_t*>(rows);
   g2.ldo = size_t(d->d) * (rows_bf16 ? 2 : 4);
   g2.out_bf16 = rows_bf16;
-  st = routed ? run_routed(g2, d, el, 1, EPI_SUM, f.partial, s, ev2, p.cap2)
-              : run_dense(g2, d->T, el, 1, EPI_SUM, f.partial, s, ev2, p.cap2);
-  if (st != MOE_OK) return st;
+  if (part2 != PART_NONE) {
+    st = routed ? run_routed(g2, d, el, 1, EPI_SUM, f.partial, s, ev2, p.cap2, part2)
+                : run_dense(g2, d->T, el, 1, EPI_SUM, f.partial, s, ev2, p.cap2);
+    if (st != MOE_OK) return st;
+  }
   return MOE_OK;
 }
 
@@ -743,6 +772,7 @@ moe_status moe_layer(const moe_desc* d, const moe_weights* w, const void* x, voi
   // the caller's second stream, when one is given, before routing starts.
   const bool fork = d->T > 0 && d->shared_inter > 0 && A.stream2 && A.ev_fork && A.ev_join;
   const bool quant = d->T > 0 && w8a8(d);
+  const bool apart = fork && routed_parts_apart(d);
   hipStream_t s2 = static_cast<hipStream_t>(A.stream2);
   hipEvent_t ev_join = static_cast<hipEvent_t>(A.ev_join);
   if (fork) {
@@ -757,8 +787,10 @@ moe_status moe_layer(const moe_desc* d, const moe_weights* w, const void* x, voi
       if (st != MOE_OK) return st;
       HIP_TRY(hipEventRecord(ev_join, s2));
     }
+    // (with the routed products apart, the shared down product is enqueued
+    // later, after the small experts' down product)
     st = run_ffn(d, shared_caps(shared_plan(d, w)), x, L.shared, L.shared_rows, rb, s2, nullptr, nullptr, nullptr,
-                 nullptr);
+                 nullptr, PART_ALL, apart ? PART_NONE : PART_ALL);
     if (st != MOE_OK) return st;
   } else if (quant) {
     st = run_quant_x(d, x, L.routed, s);
@@ -770,15 +802,33 @@ moe_status moe_layer(const moe_desc* d, const moe_weights* w, const void* x, voi
   }
   HIP_TRY(launch_permute(idx, d->T * d->k, d->E, counts, offsets, sorted_slot, slot_pos, L.chunk_hist, s));
   if (d->T == 0) return MOE_OK;
-  if (d->n_ffn > 0) {
+  const hipEvent_t e1b = static_cast<hipEvent_t>(A.ev_ffn1_begin), e1e = static_cast<hipEvent_t>(A.ev_ffn1_end);
+  const hipEvent_t e2b = static_cast<hipEvent_t>(A.ev_ffn2_begin), e2e = static_cast<hipEvent_t>(A.ev_ffn2_end);
+  const FfnPlan rp = routed_caps(routed_plan(d, w, offsets, sorted_slot));
+  if (apart) {
+    // Prefill with a second stream: the down product of the experts with at
+    // most 64 rows (weight streaming) runs on stream2 between the shared
+    // gate/up and the shared down, beside the larger experts' gate/up
+    // (matrix-core bound) on `stream`. ev_fork, recorded again after the
+    // small experts' gate/up, orders it after their h.
+    st = run_ffn(d, rp, x, L.routed, L.rows, rb, s, e1b, nullptr, nullptr, nullptr, PART_SMALL, PART_NONE);
+    if (st != MOE_OK) return st;
+    HIP_TRY(hipEventRecord(static_cast<hipEvent_t>(A.ev_fork), s));
+    st = run_ffn(d, rp, x, L.routed, L.rows, rb, s, nullptr, e1e, e2b, e2e, PART_LARGE, PART_LARGE);
+    if (st != MOE_OK) return st;
+    HIP_TRY(hipStreamWaitEvent(s2, static_cast<hipEvent_t>(A.ev_fork), 0));
+    st = run_ffn(d, rp, x, L.routed, L.rows, rb, s2, nullptr, nullptr, nullptr, nullptr, PART_NONE, PART_SMALL);
+    if (st != MOE_OK) return st;
+    st = run_ffn(d, shared_caps(shared_plan(d, w)), x, L.shared, L.shared_rows, rb, s2, nullptr, nullptr, nullptr,
+                 nullptr, PART_NONE, PART_ALL);
+    if (st != MOE_OK) return st;
+  } else if (d->n_ffn > 0) {
     if (fork && quant) HIP_TRY(hipStreamWaitEvent(s, ev_join, 0));   // the codes of x
-    st = run_ffn(d, routed_caps(routed_plan(d, w, offsets, sorted_slot)), x, L.routed, L.rows, rb, s,
-                 static_cast<hipEvent_t>(A.ev_ffn1_begin), static_cast<hipEvent_t>(A.ev_ffn1_end),
-                 static_cast<hipEvent_t>(A.ev_ffn2_begin), static_cast<hipEvent_t>(A.ev_ffn2_end));
+    st = run_ffn(d, rp, x, L.routed, L.rows, rb, s, e1b, e1e, e2b, e2e);
     if (st != MOE_OK) return st;
   }
   if (fork) {
-    HIP_TRY(hipEventRecord(ev_join, s2));   // after the shared expert on stream2
+    HIP_TRY(hipEventRecord(ev_join, s2));   // after the shared expert (and small-expert down) on stream2
     HIP_TRY(hipStreamWaitEvent(s, ev_join, 0));
   } else if (d->shared_inter > 0) {
     st = run_ffn(d, shared_caps(shared_plan(d, w)), x, L.shared, L.shared_rows, rb, s, nullptr, nullptr, nullptr,
