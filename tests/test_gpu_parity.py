@@ -724,16 +724,19 @@ def test_layer_sort_boundary(T):
     assert np.array_equal(U.np_of(t2["sorted_slot"]), np.argsort(flat, kind="stable"))
 
 
-@pytest.mark.parametrize("name", ["longcat_zero_bf16", "dsv3_decode_share_bf16"])
-def test_layer_graph_replay(name):
+@pytest.mark.parametrize("name,T", [("longcat_zero_bf16", None), ("dsv3_decode_share_bf16", None),
+                                    ("pangu_moge_w8a8", None), ("prefill_zipf_bf16", 2048)])
+def test_layer_graph_replay(name, T):
     """moe_layer captured into a HIP graph (with the shared expert forked onto
     a second stream inside the capture where there is one) replays to the
     eager result bit for bit; new inputs are copied into the captured input
-    buffer between replays, with eager work and synchronisations between."""
+    buffer between replays, with eager work and synchronisations between.
+    W8A8 records ev_join twice on the second stream, prefill sizes ev_fork
+    twice (the small experts' down product on the second stream)."""
     L, DeviceLayer, to_device = _L()
     from moe_expert_layer_fp32_amd.layer import SecondStream
-    cfg, inp = U.inputs(name)
-    lay = U.device_layer(name)
+    cfg, inp = U.inputs(name, T)
+    lay = U.device_layer(name, T)
     second = SecondStream() if cfg.shared_inter else None
     xs = [lay.x.clone(), lay.x.flip(0).contiguous()]
     eager = [lay.layer(x=xi, second=second) for xi in xs]
