@@ -7,19 +7,9 @@
  * tiles when it has many), zero-computation identity experts, the shared
  * expert, and the weighted combine back into token order.
  *
- * Sources, cited by page title and section (the pages give no formula; the
- * readings taken where they are silent are listed with the oracle):
- *  - Router Matmul, QuantBatchMatmul: page "基于Atlas 900 A3 SuperPoD的
- *    LongCat-Flash模型推理性能优化实践", section 优化措施三 (权重预取).
- *  - Zero-computation experts: same page, section 背景介绍; and page
- *    "LongCat-Flash与GLM-4.6V ...", section 拆解MoE困局.
- *  - Grouped experts (MoGE), SwiftGMM's GEMV/GEMM switch by per-expert load:
- *    page "华为技术披露集 VOL.12：昇腾×盘古", opening section and section
- *    SwiftGMM.
- *  - InitialRouting (sort all tokens by expert) and Dispatch/Combine: page on
- *    DeepSeek-V3/R1 on Ascend (Huxiu), section MOE 算子优化.
- *  - One card's share: 8 routed + 1 shared expert per card, same page,
- *    opening section.
+ * Each declaration below cites, by page title and section, the passage that
+ * defines the operation it performs. The pages give no formula of the layer;
+ * where they are silent the reading taken is stated at the declaration.
  *
  * Conventions for every entry point
  *  - Every tensor pointer is DEVICE memory owned by the caller. The library
@@ -84,6 +74,16 @@ typedef int32_t moe_status;
 
 /*
  * Layer descriptor (host memory, read during the call only).
+ *
+ * Sources: sparse activation (each token uses k of E experts) and the
+ * zero-computation experts, page "LongCat-Flash与GLM-4.6V，昇腾CANN异构计算深水区
+ * 突围详解", section 拆解MoE困局; grouped experts with one quota per group
+ * (MoGE), page "华为技术披露集 VOL.12：昇腾×盘古", opening section; one
+ * device's share of the routed experts next to one shared expert ("8 routed
+ * + 1 shared per card"), page on DeepSeek-V3/R1 on Ascend (Huxiu), opening
+ * section. Readings where the pages are silent: the softmax / sigmoid gate
+ * is a descriptor field; the group score is the sum of a group's two largest
+ * scores; ties go to the lower id.
  *
  * Selection rules (exactly one applies):
  *  - plain: n_group == 1 (or topk_group == 0 and per_group_k == 0): the k
@@ -247,6 +247,7 @@ const char* moe_status_str(moe_status status);
 size_t moe_packed_bytes(const moe_desc* desc, int part);
 
 /*
+ * (A layout conversion of this implementation, not a step of the layer.)
  * Convert one weight part from its logical layout into the packed layout the
  * kernels stream (fragment-major tiles of 16 output columns, each fragment
  * laid out as one matrix-core operand, so a wavefront reads 1 KiB of
@@ -264,15 +265,28 @@ moe_status moe_pack_weights(const moe_desc* desc, int part, const void* src_a,
 
 /*
  * Router matmul + gating + top-k.
- * x: [T][d] (fp32 for MOE_DTYPE_F32, else bf16).
- * Out: topk_idx [T][k] int32 expert ids; topk_w [T][k] fp32 gate weights.
+ * Sources: the Router Matmul is one of the weight-streaming operators of
+ * page "基于Atlas 900 A3 SuperPoD的LongCat-Flash模型推理性能优化实践", section
+ * 优化措施三; selection of k experts per token, page "LongCat-Flash与GLM-4.6V
+ * ...", section 拆解MoE困局; per-group quota (MoGE), page "华为技术披露集
+ * VOL.12：昇腾×盘古", opening section. Rules: see moe_desc.
+ * x: [T][d] (fp32 for MOE_DTYPE_F32, else bf16), device.
+ * Out: topk_idx [T][k] int32 expert ids, selections of a token in descending
+ * score order; topk_w [T][k] fp32 gate weights. Both device, caller-owned.
+ * Logits are fp32-accurate (bf16 x times three exact bf16 planes of W_r).
+ * Workspace: moe_workspace_bytes(desc, MOE_OP_ROUTE_TOPK) bytes of device
+ * memory. Errors: MOE_ERR_INVALID_ARG (null router, outputs, or x with
+ * T > 0), MOE_ERR_WORKSPACE, MOE_ERR_HIP; nothing is launched on error.
  */
 moe_status moe_route_topk(const moe_desc* desc, const moe_weights* w,
                           const void* x, int32_t* topk_idx, float* topk_w,
                           void* ws, size_t ws_bytes, void* stream);
 
 /*
- * Stable counting sort of the T*k slots (slot s = t*k + j) by expert id.
+ * Stable counting sort of the T*k slots (slot s = t*k + j) by expert id:
+ * the InitialRouting step that orders every token by expert before tokens
+ * move to their experts, page on DeepSeek-V3/R1 on Ascend (Huxiu), section
+ * MOE 算子优化. All pointers device, caller-owned.
  * Out: counts [E] (slots per expert), offsets [E+1] (exclusive prefix sum),
  * sorted_slot [T*k] (slots in ascending (expert, s) order), slot_pos [T*k]
  * (inverse: sorted_slot[slot_pos[s]] == s). An id outside [0, E) is dropped:
@@ -289,12 +303,25 @@ moe_status moe_permute(const moe_desc* desc, const int32_t* topk_idx,
  * Grouped SwiGLU FFN. MOE_FFN_ROUTED: for each resident expert e and each
  * sorted row r in [offsets[e], offsets[e+1]), token t = sorted_slot[r] / k,
  * rows[r - offsets[ffn_begin]] = W2_e^T (silu(x_t W1_e) * (x_t W3_e)).
- * Rows with fewer tokens are streamed weight-first (each weight byte read
- * once); experts with many tokens run as MFMA tiles; the choice is made on
- * the device from the offsets. MOE_FFN_SHARED: the shared expert for every
+ * Sources: the grouped matmul over the experts and SwiftGMM's switch between
+ * a weight-streaming (GEMV) and a tiled (GEMM) mode by per-expert load, page
+ * "华为技术披露集 VOL.12：昇腾×盘古", section SwiftGMM; the SwiGLU form
+ * (W1 gate, W3 up, W2 down) is a reading (the pages name no FFN form).
+ * The mode is chosen per expert on the device from the offsets (no count
+ * reaches the host): below 1024 tokens every expert streams its weights
+ * through 64-row matrix-core tiles (an expert with more rows takes several),
+ * and when the experts alone give too few workgroups the reduction is split
+ * over workgroups; from 1024 tokens up, experts with at most 64 rows stream
+ * their weights through 64-row tiles and larger experts run 128-row tiles.
+ * Shapes that do not tile (a reduction length that is not a whole number of
+ * 256-byte rows, i.e. of 128 bf16, 256 int8 or 64 fp32 elements) use one
+ * streaming kernel of 32-row tiles for every expert. MOE_FFN_SHARED: the shared expert
+ * (page on DeepSeek-V3/R1 on Ascend (Huxiu), opening section) for every
  * token, rows[t] (offsets, sorted_slot ignored).
  * x: [T][d] (fp32 or bf16 by dtype; W8A8 quantises it per token inside).
  * rows: fp32, capacity T*k rows (routed) or T rows (shared), d columns.
+ * All pointers device, caller-owned. Errors: MOE_ERR_INVALID_ARG (null x,
+ * rows, weights, or routed tables), MOE_ERR_WORKSPACE, MOE_ERR_HIP.
  */
 moe_status moe_grouped_ffn(const moe_desc* desc, const moe_weights* w,
                            int which, const void* x, const int32_t* offsets,
@@ -307,7 +334,16 @@ moe_status moe_grouped_ffn(const moe_desc* desc, const moe_weights* w,
  * rows[slot_pos[t*k+j] - offsets[ffn_begin]] for a resident FFN expert,
  * x[t] for an identity expert and 0 otherwise; fp32 sums in slot order,
  * rounded once to y's type (fp32 for MOE_DTYPE_F32, else bf16).
- * shared_rows may be NULL (no shared expert).
+ * Sources: the Combine of the Dispatch/Combine pair, page on DeepSeek-V3/R1
+ * on Ascend (Huxiu), section MOE 算子优化; a zero-computation expert returns
+ * its input, page "LongCat-Flash与GLM-4.6V ...", section 拆解MoE困局; the
+ * shared expert is added with weight 1 (a reading: the pages show no gate
+ * on it).
+ * All pointers device, caller-owned. With T > 0, x, topk_idx, topk_w,
+ * offsets [E+1], slot_pos [T*k] and y are required for every n_ffn (the
+ * kernel reads offsets[ffn_begin] and each selection's slot_pos), rows when
+ * n_ffn > 0 and shared_rows when shared_inter > 0 (else it may be NULL);
+ * a missing one is MOE_ERR_INVALID_ARG, returned before anything launches.
  */
 moe_status moe_combine(const moe_desc* desc, const void* x, const float* rows,
                        const float* shared_rows, const int32_t* topk_idx,
@@ -315,7 +351,8 @@ moe_status moe_combine(const moe_desc* desc, const void* x, const float* rows,
                        const int32_t* slot_pos, void* y, void* stream);
 
 /*
- * The whole layer in one call: (W8A8: quantise x) -> route_topk -> permute
+ * The whole layer in one call (the sources of each step are cited at the
+ * separate entry points above): (W8A8: quantise x) -> route_topk -> permute
  * -> routed FFN -> shared FFN (on aux->stream2 when given, overlapping the
  * rest) -> combine. x: [T][d]; y: [T][d] (types as in moe_combine). aux may
  * be NULL. The arithmetic is that of the separate entry points, except that

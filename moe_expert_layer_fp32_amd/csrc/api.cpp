@@ -720,8 +720,10 @@ moe_status moe_combine(const moe_desc* d, const void* x, const float* rows, cons
   moe_status st = validate(d);
   if (st != MOE_OK) return st;
   if (d->T == 0) return MOE_OK;
-  if (!x || !topk_idx || !topk_w || !y) return MOE_ERR_INVALID_ARG;
-  if (d->n_ffn > 0 && (!rows || !offsets || !slot_pos)) return MOE_ERR_INVALID_ARG;
+  // The kernel reads offsets[ffn_begin] and slot_pos for every selection,
+  // whatever n_ffn is, so both tables are required for every call with tokens.
+  if (!x || !topk_idx || !topk_w || !y || !offsets || !slot_pos) return MOE_ERR_INVALID_ARG;
+  if (d->n_ffn > 0 && !rows) return MOE_ERR_INVALID_ARG;
   if (d->shared_inter > 0 && !shared_rows) return MOE_ERR_INVALID_ARG;
   const CombineArgs c = combine_args(d, x, rows, d->shared_inter > 0 ? shared_rows : nullptr, false, topk_idx, topk_w,
                                      offsets, slot_pos, y);

@@ -15,15 +15,18 @@
 // fragment load is one contiguous 1 KiB read - and
 // never shares them, so each weight byte of a tile is read exactly once; the
 // loads run a fixed number of steps ahead of the matrix cores, which is what
-// keeps enough bytes in flight for HBM. An expert with few tokens therefore
-// runs as a weight stream whose matrix-core work only covers the
-// ceil(n_e/16) row blocks it has (the GEMV end of the per-expert GEMV/GEMM
-// choice of SwiftGMM, page "华为技术披露集 VOL.12：昇腾×盘古", section
-// SwiftGMM); experts with many rows go to the tiled GEMM of gemm_lds.hip (the
-// GEMM end). Which expert gets how many tiles is decided on the device from
-// the routing offsets, so no count ever travels to the host. The activation
-// rows (the "left matrix" SwiftGMM loads once and keeps resident) are the
-// small operand, re-read from L2.
+// keeps enough bytes in flight for HBM. An expert's matrix-core work only
+// covers the ceil(n_e/16) row blocks it has, so this is a weight stream in
+// the sense of SwiftGMM's GEMV mode (page "华为技术披露集 VOL.12：昇腾×盘古",
+// section SwiftGMM). The host picks this kernel from the shape alone: dense
+// products of at most 64 rows and products whose reduction is not a whole
+// number of 256-byte rows (which the tiled kernel of gemm_lds.hip cannot
+// stage); every other product, routed or dense, goes to the tiled kernel,
+// where the per-expert choice between its 64-row and 128-row tiles is made
+// on the device. Which expert gets how many tiles is decided on the device
+// from the routing offsets, so no count ever travels to the host. The
+// activation rows (the "left matrix" SwiftGMM loads once and keeps resident)
+// are the small operand, re-read from L2.
 #include "common.h"
 #include "kernels.h"
 

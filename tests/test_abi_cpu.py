@@ -184,3 +184,21 @@ def test_pack_rejects_small_destination(L):
     assert lib.moe_pack_weights(ctypes.byref(d), L.PACK_W13, FAKE, FAKE, FAKE, need - 1, None) == -3
     assert lib.moe_pack_weights(ctypes.byref(d), L.PACK_W13, FAKE, None, FAKE, need, None) == -1
     assert lib.moe_pack_weights(ctypes.byref(d), 99, FAKE, FAKE, FAKE, need, None) == -1
+
+
+@pytest.mark.parametrize("n_ffn", [0, 8])
+def test_combine_requires_routing_tables_for_every_n_ffn(L, n_ffn):
+    """moe_combine reads offsets[ffn_begin] and each selection's slot_pos even
+    when no FFN expert is resident, so NULL tables are rejected on the host
+    (MOE_ERR_INVALID_ARG) before anything is launched, whatever n_ffn is."""
+    lib = L.load_library()
+    d = _desc(L, n_ffn=n_ffn, shared_inter=0)
+    rows = FAKE if n_ffn else None
+    for offsets, slot_pos in ((None, FAKE), (FAKE, None), (None, None)):
+        assert lib.moe_combine(ctypes.byref(d), FAKE, rows, None, FAKE, FAKE, offsets, slot_pos, FAKE,
+                               None) == -1, (offsets, slot_pos)
+    if n_ffn:   # the expert rows stay required with resident experts
+        assert lib.moe_combine(ctypes.byref(d), FAKE, None, None, FAKE, FAKE, FAKE, FAKE, FAKE, None) == -1
+    # with T == 0 every call is a no-op that reads nothing
+    d.T = 0
+    assert lib.moe_combine(ctypes.byref(d), None, None, None, None, None, None, None, None, None) == 0
