@@ -73,22 +73,65 @@ def logit_error_bound(x64: np.ndarray, wr64: np.ndarray, z: np.ndarray, dtype: s
 def compare_routing(cfg, ref: dict, idx_gpu: np.ndarray, w_gpu: np.ndarray, x64, wr64,
                     w_tol: float = 1e-5):
     """Exact ids and weights within w_tol for every token whose decision is
-    clear of a tie; validity only for near-tie tokens. Returns the near-tie mask."""
+    clear of a tie; for near-tie tokens, that the GPU's choice is a valid one
+    within rounding of the oracle's. Returns the near-tie mask.
+
+    Near-tie tokens must still satisfy every rule of the selection: distinct
+    ids in range; at most topk_group groups (group-limited) or exactly
+    per_group_k ids in every group (per-group quota); positive weights that
+    sum to route_scale (renormalised). And every id the GPU picked that the
+    oracle did not must lie within twice the logit error bound of the
+    oracle's boundary value: the k-th largest logit among the oracle's
+    candidates (plain and group-limited), the per_group_k-th largest logit of
+    its group (quota), or, for an id of a group the oracle dropped, a group
+    score within twice its bound of the last group the oracle kept."""
     bz = logit_error_bound(x64, wr64, ref["z"], cfg.dtype)
+    bg = 2 * (0.5 * bz + 1e-6)                 # group scores: sigmoid slope <= 1/4, two scores summed
     mz, mg = O.selection_margins(ref["z"], ref["scores"], cfg)
-    amb = (mz <= 2 * bz) | (mg <= 2 * (0.5 * bz + 1e-6))
+    amb = (mz <= 2 * bz) | (mg <= bg)
     clear = ~amb
     bad = np.argwhere(idx_gpu[clear] != ref["idx"][clear])
     assert bad.size == 0, (f"{bad.shape[0]} id mismatches on clear tokens; first token "
                            f"{np.flatnonzero(clear)[bad[0][0]]}")
     werr = np.abs(w_gpu[clear] - ref["w"][clear]).max() if clear.any() else 0.0
     assert werr <= w_tol, f"gate weight error {werr}"
+    gsize = cfg.E // cfg.n_group
     for t in np.flatnonzero(amb):
         row = idx_gpu[t]
-        assert len(set(row.tolist())) == cfg.k and row.min() >= 0 and row.max() < cfg.E
-        if not cfg.topk_group and not cfg.per_group_k:
-            kth = np.sort(ref["z"][t])[::-1][cfg.k - 1]
-            assert np.all(ref["z"][t][row] >= kth - 2 * bz[t])
+        zt, st = ref["z"][t], ref["scores"][t]
+        assert len(set(row.tolist())) == cfg.k and row.min() >= 0 and row.max() < cfg.E, f"token {t}: ids {row}"
+        assert np.all(w_gpu[t] > 0), f"token {t}: weights {w_gpu[t]}"
+        if cfg.renorm:
+            assert abs(float(w_gpu[t].sum()) - cfg.route_scale) <= 1e-6 * max(1.0, cfg.route_scale), \
+                f"token {t}: weights sum {w_gpu[t].sum()}"
+        groups = row // gsize
+        oracle_row = set(ref["idx"][t].tolist())
+        swapped = [int(e) for e in row if int(e) not in oracle_row]
+        if cfg.per_group_k:
+            assert np.array_equal(np.bincount(groups, minlength=cfg.n_group),
+                                  np.full(cfg.n_group, cfg.per_group_k)), f"token {t}: quota {row}"
+            for e in swapped:
+                g = e // gsize
+                bound = np.sort(zt[g * gsize:(g + 1) * gsize])[::-1][cfg.per_group_k - 1]
+                assert zt[e] >= bound - 2 * bz[t], f"token {t}: id {e} far from its group's boundary"
+            continue
+        if cfg.topk_group:
+            assert len(set(groups.tolist())) <= cfg.topk_group, f"token {t}: groups {groups}"
+            gscore = np.array([O.group_score(st[g * gsize:(g + 1) * gsize]) for g in range(cfg.n_group)])
+            kept = set(sorted(range(cfg.n_group), key=lambda g: (-gscore[g], g))[: cfg.topk_group])
+            last_kept = min(gscore[g] for g in kept)
+            cand = np.concatenate([zt[g * gsize:(g + 1) * gsize] for g in sorted(kept)])
+            kth = np.sort(cand)[::-1][cfg.k - 1]
+            for e in swapped:
+                g = e // gsize
+                if g in kept:
+                    assert zt[e] >= kth - 2 * bz[t], f"token {t}: id {e} far from the k boundary"
+                else:
+                    assert gscore[g] >= last_kept - bg[t], f"token {t}: group {g} far from the kept groups"
+            continue
+        kth = np.sort(zt)[::-1][cfg.k - 1]
+        for e in swapped:
+            assert zt[e] >= kth - 2 * bz[t], f"token {t}: id {e} far from the k boundary"
     return amb
 
 

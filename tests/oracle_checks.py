@@ -248,9 +248,32 @@ def all_checks(O):
     bad += check_golden_w8a8_parts(O)
     bad += check_brute_force(O)
     bad += check_routing_tables(O)
+    bad += check_selection_margins(O)
     return bad
 
 
 def quantised_weight(rng, K, N):
     """int8 weight + per-column scale of a random [K, N] fp32 matrix."""
     return quantise_weight_int8(rng.standard_normal((K, N)).astype(np.float32) * np.float32(0.02))
+
+
+def check_selection_margins(O):
+    """Hand-worked margins (tests/golden/selection_margins.json) of the plain,
+    group-limited and per-group-quota rules; scores are taken from the
+    library's softmax / logistic functions (scipy), not from the oracle."""
+    import scipy.special as sps
+    raw = G.load("selection_margins.json")
+    bad = []
+    for case in raw["cases"]:
+        cfg = MoEConfig(**case["cfg"])
+        cfg.check()
+        z = np.asarray(case["z"], np.float64)
+        s = sps.softmax(z, axis=1) if cfg.gate == "softmax" else sps.expit(z)
+        mz, mg = O.selection_margins(z, s, cfg)
+        want_z = np.asarray(G.value(case["expected"]["mz"]), np.float64)
+        want_g = np.asarray([np.inf if v is None else G.value(v) for v in case["expected"]["mg"]], np.float64)
+        if mz.shape != want_z.shape or not np.allclose(mz, want_z, rtol=1e-12, atol=1e-15):
+            bad.append(f"margins {cfg.name}: mz {mz.tolist()} != {want_z.tolist()}")
+        if mg.shape != want_g.shape or not np.allclose(mg, want_g, rtol=1e-12, atol=1e-15):
+            bad.append(f"margins {cfg.name}: mg {mg.tolist()} != {want_g.tolist()}")
+    return bad

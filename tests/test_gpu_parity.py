@@ -410,7 +410,12 @@ def test_grouped_ffn_shared(name):
 # combine on given rows
 # ----------------------------------------------------------------------------
 @pytest.mark.parametrize("name", ["tiny_fp32", "longcat_zero_bf16"])
-def test_combine(name):
+@pytest.mark.parametrize("with_shared", [False, True])
+def test_combine(name, with_shared):
+    """moe_combine on given expert rows (random), its own routing tables, and
+    (with_shared) a given shared-expert row per token: y = shared + the
+    weighted rows of resident experts + the weighted x of identity experts,
+    against the same sum written out in fp64."""
     L, DeviceLayer, to_device = _L()
     cfg, inp = U.inputs(name)
     lay = U.device_layer(name)
@@ -418,11 +423,17 @@ def test_combine(name):
     rng = np.random.default_rng(22)
     R = cfg.T * cfg.k
     rows = rng.standard_normal((R, cfg.d)).astype(np.float32)
-    shared = rng.standard_normal((cfg.T, cfg.d)).astype(np.float32)
-    U.say(f"[gpu] combine {name}")
+    shared = rng.standard_normal((cfg.T, cfg.d)).astype(np.float32) if with_shared else None
+    U.say(f"[gpu] combine {name} shared={with_shared}")
     counts, offsets, ss, sp = lay.permute(torch.from_numpy(idx).cuda())
-    y = lay.combine(torch.from_numpy(rows).cuda(), None, torch.from_numpy(idx).cuda(),
-                    torch.from_numpy(w).cuda(), offsets, sp)
+    # the shared rows are read only when the descriptor has a shared expert
+    desc = L.desc_from_config(cfg.replace(shared_inter=64) if with_shared else cfg)
+    xdev = lay.x
+    y = torch.empty((cfg.T, cfg.d), dtype=lay.xdtype, device="cuda")
+    L.moe_combine(desc, xdev, torch.from_numpy(rows).cuda(),
+                  torch.from_numpy(shared).cuda() if with_shared else None, torch.from_numpy(idx).cuda(),
+                  torch.from_numpy(w).cuda(), offsets, sp, y)
+    torch.cuda.synchronize()
     _, off_ref, _, sp_ref = O.routing_tables(idx, cfg.E)
     x = np.asarray(O.x_f32(inp), np.float64)
     Uu = np.zeros((cfg.T, cfg.k, cfg.d))
@@ -434,10 +445,12 @@ def test_combine(name):
                 Uu[t, j] = rows[sp_ref[t * cfg.k + j] - off_ref[cfg.ffn_begin]]
             elif kind == "identity":
                 Uu[t, j] = x[t]
-    want = O.weighted_sum(Uu, w, None)
+    want = O.weighted_sum(Uu, w, None if shared is None else shared.astype(np.float64))
     _, beyond = U.output_errors(U.np_of(y), want, cfg.dtype)
     assert beyond <= 1e-6
-    del shared
+    if with_shared:   # the shared rows really entered the sum
+        _, without = U.output_errors(U.np_of(y), O.weighted_sum(Uu, w, None), cfg.dtype)
+        assert without > 0.1
 
 
 @pytest.mark.parametrize("T,skew", [(2048, 0.0), (2100, 1.5)])
@@ -506,13 +519,31 @@ def _check_layer(cfg, inp, lay, tokens=None, ws=None, second=None, tuning=None):
     amb = U.compare_routing(cfg, ref, idx_gpu[sel], w_gpu[sel], x64, inp["w_router"].astype(np.float64))
     assert amb.mean() < 0.05
     clear = ~amb
-    y_gpu = U.np_of(y)[sel][clear]
+    y_all = U.np_of(y)[sel]
+    y_gpu = y_all[clear]
     lit, beyond = U.output_errors(y_gpu, ref["y"][clear], cfg.dtype)
+    # Near-tie tokens: the oracle rerun on the GPU's own ids (downstream on
+    # identical top-k indices), weights and outputs compared on every one.
+    beyond_amb = 0.0
+    if amb.any():
+        tok_all = np.arange(cfg.T)[sel]
+        amb_tok = tok_all[amb]
+        ref_amb = O.moe_layer(inp, cfg, tokens=amb_tok, topk_idx=idx_gpu[sel][amb])
+        werr = float(np.abs(w_gpu[sel][amb] - ref_amb["w"]).max())
+        assert werr <= 1e-5, f"near-tie gate weights under identical ids: {werr}"
+        # rms of the whole compared batch, so a handful of tokens is measured
+        # on the same scale as the rest
+        rms_all = float(np.sqrt(np.mean(ref["y"][clear] ** 2))) if clear.any() else 1.0
+        diff = np.abs(y_all[amb] - ref_amb["y"])
+        allow = U.half_ulp(np.maximum(np.abs(ref_amb["y"]), np.abs(y_all[amb])), cfg.dtype)
+        beyond_amb = float(np.maximum(diff - allow, 0).max() / rms_all)
     U.say(f"    {cfg.name} T={cfg.T}: max|err|/rms literal {lit:.3e} beyond-rounding {beyond:.3e} "
-          f"near-tie tokens {int(amb.sum())}")
+          f"near-tie tokens {int(amb.sum())} (their error under identical ids {beyond_amb:.3e})")
     U.record(test="layer", cfg=cfg.name, T=cfg.T, sampled=None if tokens is None else len(tokens),
-             err_literal=lit, err_beyond_rounding=beyond, near_tie_tokens=int(amb.sum()))
+             err_literal=lit, err_beyond_rounding=beyond, near_tie_tokens=int(amb.sum()),
+             near_tie_err_beyond_rounding=beyond_amb)
     assert beyond <= U.TOL[cfg.dtype]
+    assert beyond_amb <= U.TOL[cfg.dtype]
     # routing tables of the layer are the stable sort of its own ids
     counts, offsets, ss, sp = (U.np_of(t[n]) for n in ("counts", "offsets", "sorted_slot", "slot_pos"))
     flat = idx_gpu.reshape(-1)
@@ -538,14 +569,69 @@ def test_layer(name, T):
     _check_layer(cfg, inp, lay)
 
 
-def test_layer_prefill_sampled_tokens():
-    """The full prefill workload (T 8192, 32 of 256 experts resident, Zipf
-    popularity) on the GPU, checked on 48 sampled tokens by the oracle."""
+PREFILL_SAMPLED_TOKENS = 512
+
+
+def test_layer_prefill_full_size():
+    """The full prefill workload (T 8192, d 7168, 32 of 256 experts resident,
+    Zipf popularity) in the launch configuration bench.py times (shared
+    expert on a second stream), against the oracle:
+    - the ids of all 8192 tokens (exact where clear of a tie, valid within
+      rounding where not) and their gate weights;
+    - the layer output on 512 sampled tokens (near-tie tokens under the
+      GPU's own ids);
+    - every expert output row (moe_aux.rows) of the largest resident expert,
+      the smallest non-empty one, and the experts either side of the 64-row
+      split (64-row weight-streaming tiles below, 128-row tiles above), at
+      K = 7168, against the oracle's FFN of the same tokens."""
+    from moe_expert_layer_fp32_amd.layer import SecondStream
     cfg, inp = U.inputs("prefill_zipf_bf16")
     lay = U.device_layer("prefill_zipf_bf16")
-    U.say("[gpu] layer prefill_zipf_bf16 T=8192 (sampled)")
-    toks = np.random.default_rng(5).choice(cfg.T, 48, replace=False)
-    _check_layer(cfg, inp, lay, tokens=np.sort(toks))
+    U.say("[gpu] layer prefill_zipf_bf16 T=8192 (full size, two streams, intermediates)")
+    y, t = lay.layer_with_tables(second=SecondStream(), intermediates=True)
+    torch.cuda.synchronize()
+    idx_gpu, w_gpu = U.np_of(t["topk_idx"]), U.np_of(t["topk_w"])
+    x64, wr64 = U.x64_of(inp), inp["w_router"].astype(np.float64)
+    U.say("    oracle routing of all 8192 tokens")
+    z, sc, idx, w = O.route(inp, cfg)
+    amb = U.compare_routing(cfg, dict(z=z, scores=sc, idx=idx, w=w), idx_gpu, w_gpu, x64, wr64)
+    assert amb.mean() < 0.05
+    U.record(test="prefill_full_size_routing", tokens=cfg.T, near_tie_tokens=int(amb.sum()))
+
+    # layer output on sampled tokens, downstream on the GPU's own ids
+    toks = np.sort(np.random.default_rng(5).choice(cfg.T, PREFILL_SAMPLED_TOKENS, replace=False))
+    U.say(f"    oracle layer on {toks.size} sampled tokens")
+    ref = O.moe_layer(inp, cfg, tokens=toks, topk_idx=idx_gpu[toks])
+    y_s = U.np_of(y)[toks]
+    lit, beyond = U.output_errors(y_s, ref["y"], cfg.dtype)
+    U.say(f"    sampled output: literal {lit:.3e} beyond rounding {beyond:.3e}")
+    U.record(test="prefill_full_size_output", sampled=int(toks.size), err_literal=lit, err_beyond_rounding=beyond)
+    assert beyond <= U.TOL[cfg.dtype]
+
+    # expert output rows of chosen experts, every row
+    counts, offsets, ss = (U.np_of(t[n]) for n in ("counts", "offsets", "sorted_slot"))
+    res = counts[cfg.ffn_begin:cfg.ffn_begin + cfg.n_ffn]
+    nz = np.flatnonzero(res > 0)
+    small = nz[res[nz] <= 64]
+    large = nz[res[nz] > 64]
+    pick = {"largest": int(nz[np.argmax(res[nz])]), "smallest": int(nz[np.argmin(res[nz])])}
+    if small.size:
+        pick["largest <= 64 rows"] = int(small[np.argmax(res[small])])
+    if large.size:
+        pick["smallest > 64 rows"] = int(large[np.argmin(res[large])])
+    base = offsets[cfg.ffn_begin]
+    X32 = np.asarray(O.x_f32(inp), np.float32)
+    for what, el in pick.items():
+        e = cfg.ffn_begin + el
+        r0, r1 = offsets[e], offsets[e + 1]
+        tokens = ss[r0:r1] // cfg.k
+        U.say(f"    rows of expert {e} ({what}, {r1 - r0} rows)")
+        got = U.np_of(t["rows"][r0 - base:r1 - base])
+        want = O.expert_ffn(inp, cfg, el, X32[tokens])
+        lit_r, beyond_r = U.output_errors(got, want, "bf16")
+        U.record(test="prefill_full_size_rows", expert=e, which=what, rows=int(r1 - r0), err_literal=lit_r,
+                 err_beyond_rounding=beyond_r)
+        assert beyond_r <= U.TOL["bf16"], f"expert {e} ({what}): {beyond_r}"
 
 
 def _f32(v):

@@ -101,10 +101,35 @@ def _softmax_without_max_shift_but_wrong_axis(z, gate):
     return _orig_scores(z, gate)
 
 
+def _margins_group_gap_wrong_index(z, scores, cfg):
+    """Group gap taken one place too late (between the first and second
+    dropped groups instead of the last kept and the first dropped)."""
+    mz, mg = _orig_margins(z, scores, cfg)
+    if cfg.topk_group and cfg.topk_group + 1 < cfg.n_group:
+        gsize = cfg.E // cfg.n_group
+        for t in range(z.shape[0]):
+            gs = sorted((sum(sorted(scores[t, g * gsize:(g + 1) * gsize], reverse=True)[:2])
+                         for g in range(cfg.n_group)), reverse=True)
+            mg[t] = gs[cfg.topk_group] - gs[cfg.topk_group + 1]
+    return mz, mg
+
+
+def _margins_moge_ignoring_groups(z, scores, cfg):
+    """Per-group quota margin taken over the global k + 1 largest logits, as
+    if there were no group boundaries."""
+    mz, mg = _orig_margins(z, scores, cfg)
+    if cfg.per_group_k:
+        for t in range(z.shape[0]):
+            v = sorted(z[t], reverse=True)[: cfg.k + 1]
+            mz[t] = min(v[i] - v[i + 1] for i in range(len(v) - 1))
+    return mz, mg
+
+
 _orig_swiglu = O.swiglu
 _orig_kind = O.expert_kind
 _orig_tables = O.routing_tables
 _orig_scores = O.gate_scores
+_orig_margins = O.selection_margins
 
 MUTANTS = {
     "silu sign flipped": ("silu", _silu_wrong_sign),
@@ -122,6 +147,8 @@ MUTANTS = {
     "int8 rounding half away from zero": ("quantise_rows", _quantise_half_away),
     "int8 scale amax/128": ("quantise_rows", _quantise_scale_128),
     "softmax over the wrong axis": ("gate_scores", _softmax_without_max_shift_but_wrong_axis),
+    "group gap taken at the wrong index": ("selection_margins", _margins_group_gap_wrong_index),
+    "per-group margin ignores the group boundaries": ("selection_margins", _margins_moge_ignoring_groups),
 }
 
 

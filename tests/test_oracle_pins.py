@@ -30,6 +30,11 @@ def test_brute_force_dense_mixture():
     assert C.check_brute_force(O, seeds=range(120)) == []
 
 
+def test_selection_margins_hand_worked():
+    """Group-limited, per-group-quota and plain margins against hand-worked values."""
+    assert C.check_selection_margins(O) == []
+
+
 def test_routing_tables_vs_stable_argsort():
     assert C.check_routing_tables(O, seeds=range(60)) == []
 
