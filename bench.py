@@ -10,10 +10,15 @@ last-level cache from the step before; L is chosen so the L layers' weights
 exceed 1 GB. Inputs are resident in HBM before the timed region.
 
 Prints one JSON line: value = tokens/s over the K timed steps, plus the
-roofline of the dominant kernel (the routed experts' gate/up projection with
-SwiGLU: algorithmic bytes per launch / its mean duration from HIP events
-recorded on the layer's stream around every launch) and the CPU oracle's
-throughput on a bounded sample of the same workload.
+roofline of the dominant kernel and the CPU oracle's throughput on a bounded
+sample of the same workload. The dominant kernel is the largest launch of the
+call: for the prefill workload (the default, 8192 tokens) the shared expert's
+gate/up projection with SwiGLU (matrix-core bound: algorithmic flops per
+launch / its mean duration), for the decode workloads the routed experts'
+gate/up projection with SwiGLU (HBM bound: algorithmic bytes per launch / its
+mean duration). Durations come from HIP events stamped by the launch's own
+dispatch on the stream it runs on. `layer_roofline` applies the same roofline
+to the whole call.
 """
 from __future__ import annotations
 
@@ -33,7 +38,7 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0      # dense bf16 matrix cores
 INT8_PEAK_TOPS = 5000.0        # dense int8 matrix cores
 FP32_PEAK_TFLOPS = 157.3
-DEFAULT_CONFIG = "longcat_zero_bf16"
+DEFAULT_CONFIG = "prefill_zipf_bf16"
 METRIC = "MoE-layer tokens/s at 1 GPU; decode HBM GB/s %peak; prefill MFMA %peak"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "ffn1_traffic.json")
 CSRC = os.path.join(ROOT, "moe_expert_layer_fp32_amd", "csrc")
@@ -59,6 +64,12 @@ def parse():
                    help="only run 5 device copies of 1 GiB (the known-size kernel for counter calibration)")
     p.add_argument("--traffic", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "CAL_FETCH_CSV", "CAL_WRITE_CSV"),
                    help="turn rocprofv3 --pmc counter_collection.csv files into the traffic record")
+    p.add_argument("--traffic-kernel", default="",
+                   help="with --traffic: the kernel name the dominant launch has in the counter files")
+    p.add_argument("--traffic-occurrence", type=int, default=0,
+                   help="with --traffic: which dispatch of that kernel within each layer call (0 = first)")
+    p.add_argument("--traffic-per-call", type=int, default=1,
+                   help="with --traffic: dispatches of that kernel per layer call")
     return p.parse_args()
 
 
@@ -86,23 +97,29 @@ def counter_values(path: str) -> dict:
     return out
 
 
-def traffic_record(args, cfg_name: str) -> dict:
+def traffic_record(paths, cfg_name: str, kernel: str, occurrence: int, per_call: int) -> dict:
     """HBM bytes per launch of the dominant kernel from FETCH_SIZE and
     WRITE_SIZE (KiB per dispatch), each scaled by what the counter reads for a
-    device copy of COPY_BYTES bytes (read COPY_BYTES, write COPY_BYTES)."""
+    device copy of COPY_BYTES bytes (read COPY_BYTES, write COPY_BYTES). The
+    launch is the `occurrence`-th of `per_call` dispatches of `kernel` in each
+    layer call (the same kernel can serve several products of a call)."""
     import statistics
-    fetch, write, cal_f, cal_w = (counter_values(p) for p in args)
+    fetch, write, cal_f, cal_w = (counter_values(p) for p in paths)
     copy = [k for k in cal_f if "copyBuffer" in k]
     cf = statistics.median(cal_f[copy[0]]) * 1024.0
     cw = statistics.median(cal_w[copy[0]]) * 1024.0
     f_scale, w_scale = COPY_BYTES / cf, COPY_BYTES / cw
-    # the dominant kernel: the gate/up + SwiGLU instance with the most fetched bytes
-    cands = {k: v for k, v in fetch.items() if ("gemm_lds_kernel" in k or "gemm_rows_kernel" in k)
-             and (", 2, 0" in k)}
-    name = max(cands, key=lambda k: statistics.median(cands[k]))
-    fb = statistics.median(fetch[name]) * 1024.0 * f_scale
-    wb = statistics.median(write[name]) * 1024.0 * w_scale
-    return {"workload": cfg_name, "kernel": name, "kernel_sha": kernel_hash(),
+    names = [k for k in fetch if kernel and kernel in k]
+    if len(names) != 1:
+        raise SystemExit(f"--traffic-kernel {kernel!r} matches {len(names)} kernels: {names}")
+    name = names[0]
+    f_all, w_all = fetch[name], write[name]
+    f_sel = f_all[occurrence::per_call]
+    w_sel = w_all[occurrence::per_call]
+    fb = statistics.median(f_sel) * 1024.0 * f_scale
+    wb = statistics.median(w_sel) * 1024.0 * w_scale
+    return {"workload": cfg_name, "kernel": name, "occurrence": occurrence, "per_call": per_call,
+            "dispatches": len(f_sel), "kernel_sha": kernel_hash(),
             "fetch_bytes_per_launch": fb, "write_bytes_per_launch": wb,
             "bytes_per_launch": fb + wb, "fetch_scale": f_scale, "write_scale": w_scale,
             "copy_bytes": COPY_BYTES}
@@ -130,6 +147,19 @@ def ffn1_algorithmic(cfg, counts_per_layer):
     return out
 
 
+def shared_ffn1_algorithmic(cfg):
+    """Algorithmic work of one launch of the shared expert's gate/up
+    projection (dense over all T tokens): bytes = its W1 and W3, x read once
+    and h written; flops = 2 * T * d * 2 I_s."""
+    wb = {"f32": 4, "bf16": 2, "w8a8": 1}[cfg.dtype]
+    xb = {"f32": 4, "bf16": 2, "w8a8": 1}[cfg.dtype]
+    hb = {"f32": 4, "bf16": 2, "w8a8": 4}[cfg.dtype]
+    byts = 2 * cfg.d * cfg.shared_inter * wb + cfg.T * cfg.d * xb + cfg.T * cfg.shared_inter * hb
+    if cfg.dtype == "w8a8":
+        byts += 2 * cfg.shared_inter * 4
+    return byts, 2.0 * cfg.T * cfg.d * 2 * cfg.shared_inter
+
+
 def layer_algorithmic(cfg, counts_per_layer):
     """Algorithmic work of one whole layer call (the survey's count):
     bytes = W1, W3 and W2 (and int8 scales) of every resident FFN expert that
@@ -153,10 +183,45 @@ def layer_algorithmic(cfg, counts_per_layer):
     return out
 
 
+def cpu_info() -> dict:
+    """Model name and core counts of this host: physical cores (distinct
+    (physical id, core id) pairs of /proc/cpuinfo), logical CPUs, and the
+    CPUs this process may run on."""
+    model, pairs, logical = "unknown", set(), 0
+    phys = core = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                key, _, val = line.partition(":")
+                key, val = key.strip(), val.strip()
+                if key == "model name" and model == "unknown":
+                    model = val
+                elif key == "processor":
+                    logical += 1
+                elif key == "physical id":
+                    phys = val
+                elif key == "core id":
+                    core = val
+                elif not key and phys is not None:
+                    pairs.add((phys, core))
+                    phys = core = None
+        if phys is not None:
+            pairs.add((phys, core))
+    except OSError:
+        pass
+    try:
+        avail = len(os.sched_getaffinity(0))
+    except AttributeError:
+        avail = os.cpu_count() or 1
+    return {"cpu_model": model, "physical_cores": len(pairs) or None, "logical_cpus": logical or os.cpu_count(),
+            "cpus_available": avail}
+
+
 def cpu_baseline(cfg, inp, seconds: float):
-    """The oracle as it stands, timed on this host on a bounded sample."""
+    """The oracle as it stands, timed on this host on a bounded sample: once
+    with every BLAS thread numpy has, once with one thread."""
     import numpy as np
-    from threadpoolctl import threadpool_info
+    from threadpoolctl import threadpool_info, threadpool_limits
 
     from oracle import moe_oracle as O
 
@@ -164,18 +229,28 @@ def cpu_baseline(cfg, inp, seconds: float):
     if cfg.T * cfg.d * max(cfg.inter, cfg.shared_inter, 1) > 256 * 1024 * 2048:
         sample = 64
     toks = np.arange(sample)
-    t0 = time.perf_counter()
-    n = 0
-    while True:
-        O.moe_layer(inp, cfg, tokens=toks)
-        n += sample
-        el = time.perf_counter() - t0
-        if el >= seconds:
-            break
+
+    def timed(budget):
+        t0 = time.perf_counter()
+        n = 0
+        while True:
+            O.moe_layer(inp, cfg, tokens=toks)
+            n += sample
+            el = time.perf_counter() - t0
+            if el >= budget:
+                return n, el
+
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    n, el = timed(seconds)
+    with threadpool_limits(limits=1):
+        n1, el1 = timed(seconds / 2)
+    info = cpu_info()
     return {"value": n / el, "unit": "tokens/s", "cores": threads, "kind": "oracle",
             "sample": f"{n} tokens: {n // sample} oracle calls on the first {sample} tokens of the "
-                      f"{cfg.name} batch, {el:.1f} s wall, numpy fp64 with {threads} BLAS threads"}
+                      f"{cfg.name} batch, {el:.1f} s wall, numpy fp64 with {threads} BLAS threads",
+            "one_thread": {"value": n1 / el1, "unit": "tokens/s", "cores": 1,
+                           "sample": f"{n1} tokens in {n1 // sample} calls, {el1:.1f} s wall"},
+            **info}
 
 
 def graph_replay(L, layers, desc, y, ws, second, K, tuning=None):
@@ -206,7 +281,8 @@ def graph_replay(L, layers, desc, y, ws, second, K, tuning=None):
 def main() -> int:
     args = parse()
     if args.traffic:
-        rec = traffic_record(args.traffic, args.config)
+        rec = traffic_record(args.traffic, args.config, args.traffic_kernel, args.traffic_occurrence,
+                             args.traffic_per_call)
         with open(TRAFFIC_FILE, "w") as f:
             json.dump(rec, f, indent=1)
         print(json.dumps(rec))
@@ -258,11 +334,21 @@ def main() -> int:
     torch.cuda.synchronize()
 
     K, W = args.steps, args.warmup
+    prefill = cfg.T >= 4096
+    # The dominant launch: the shared expert's gate/up for the prefill
+    # workload (when it has a shared expert), else the routed gate/up.
+    dom_shared = prefill and cfg.shared_inter > 0
     # Timing events with a device-scope release (see hip_events): stamped by
-    # the gate/up kernel's own dispatch, they add no L2 write-back between
-    # kernels, so the timed steps run as untimed ones do.
+    # the launches' own dispatch, they add no L2 write-back between kernels,
+    # so the timed steps run as untimed ones do.
     ev = [(Event(), Event()) for _ in range(K)]
-    auxes = [L.MoeAux(ev_ffn1_begin=a.handle, ev_ffn1_end=b.handle) for a, b in ev]
+    ev_s = [(Event(), Event()) for _ in range(K)] if cfg.shared_inter else None
+    auxes = []
+    for i, (a, b) in enumerate(ev):
+        aux = L.MoeAux(ev_ffn1_begin=a.handle, ev_ffn1_end=b.handle)
+        if ev_s is not None:
+            aux.ev_sffn1_begin, aux.ev_sffn1_end = ev_s[i][0].handle, ev_s[i][1].handle
+        auxes.append(aux)
     second = SecondStream() if args.streams == 2 and cfg.shared_inter else None
     if second is not None:
         for a in auxes:
@@ -303,28 +389,51 @@ def main() -> int:
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
+    peak = INT8_PEAK_TOPS if cfg.dtype == "w8a8" else (FP32_PEAK_TFLOPS if cfg.dtype == "f32" else BF16_PEAK_TFLOPS)
+
+    def launch_roofline(ms, byts, flops, bound, what):
+        """Roofline object of one launch: algorithmic work per launch over
+        its mean duration from the stamped events."""
+        mean_s = float(ms.mean()) / 1e3
+        if bound == "mfma":
+            r = {"bound": "mfma", "achieved": round(float(flops.mean()) / mean_s / 1e12, 2), "peak": peak,
+                 "unit": "TFLOP/s"}
+        else:
+            r = {"bound": "hbm", "achieved": round(float(byts.mean()) / mean_s / 1e9, 1), "peak": HBM_PEAK_GBS,
+                 "unit": "GB/s"}
+        r["frac"] = round(r["achieved"] / r["peak"], 4)
+        r["kernel"] = what
+        r["mean_us"] = round(mean_s * 1e6, 2)
+        r["p10_p50_p90_us"] = [round(float(v) * 1e3, 2) for v in np.percentile(ms, [10, 50, 90])]
+        r["alg_bytes_per_launch"] = int(byts.mean())
+        r["alg_flops_per_launch"] = float(flops.mean())
+        return r
+
+    bound = "mfma" if prefill else "hbm"
     ffn1_ms = np.array([a.elapsed_ms(b) for a, b in ev])
     alg = ffn1_algorithmic(cfg, counts_per_layer)
     alg_bytes = np.array([alg[i % n_layers][0] for i in range(K)])
     alg_flops = np.array([alg[i % n_layers][1] for i in range(K)])
-    mean_s = float(ffn1_ms.mean()) / 1e3
-    prefill = cfg.T >= 4096
-    if prefill:
-        peak = INT8_PEAK_TOPS if cfg.dtype == "w8a8" else (FP32_PEAK_TFLOPS if cfg.dtype == "f32" else BF16_PEAK_TFLOPS)
-        achieved = float(alg_flops.mean()) / mean_s / 1e12
-        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s"}
+    routed_what = ("routed-expert gate/up projection + SwiGLU (" +
+                   ("two launches on the layer's stream: experts with at most 64 rows, then larger experts"
+                    if prefill else "one launch") + ")")
+    routed_roof = launch_roofline(ffn1_ms, alg_bytes, alg_flops, bound, routed_what)
+    if dom_shared:
+        sb, sf = shared_ffn1_algorithmic(cfg)
+        s_ms = np.array([a.elapsed_ms(b) for a, b in ev_s])
+        roof = launch_roofline(s_ms, np.full(K, float(sb)), np.full(K, sf), "mfma",
+                               "shared-expert gate/up projection + SwiGLU (one launch per step" +
+                               (", on the second stream beside the routed experts)" if second is not None
+                                else ")"))
+        roof_name = "shared_ffn1"
     else:
-        achieved = float(alg_bytes.mean()) / mean_s / 1e9
-        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s"}
-    roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
-    roof["kernel"] = "routed-expert gate/up projection + SwiGLU (one launch per step)"
-    roof["mean_us"] = round(mean_s * 1e6, 2)
-    roof["p10_p50_p90_us"] = [round(float(v) * 1e3, 2) for v in np.percentile(ffn1_ms, [10, 50, 90])]
-    roof["alg_bytes_per_launch"] = int(alg_bytes.mean())
+        roof = routed_roof
+        roof_name = "routed_ffn1"
     roof["traffic"] = None
     if os.path.exists(TRAFFIC_FILE):
         tr = json.load(open(TRAFFIC_FILE))
-        if tr.get("kernel_sha") == kernel_hash() and tr.get("workload") == cfg.name:
+        if tr.get("kernel_sha") == kernel_hash() and tr.get("workload") == cfg.name and \
+                tr.get("launch") == roof_name:
             roof["traffic"] = tr.get("bytes_per_launch")
 
     # The whole layer call against the same roofline: algorithmic bytes (or
@@ -369,6 +478,7 @@ def main() -> int:
                    "global_batch": cfg.T, "parallelism": "none (1 GPU)"},
         "roofline": roof,
         "layer_roofline": layer_roof,
+        **({"routed_ffn1_roofline": routed_roof} if dom_shared else {}),
         "cpu_baseline": cpu,
     }
     if tuned is not None:

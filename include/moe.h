@@ -235,6 +235,13 @@ typedef struct moe_aux {
     float* s_h;           /* W8A8: [T*k] their per-row scales */
     void* rows;           /* [T*k][d] expert output rows h W2 before the gate
                            * weights: float for F32 and W8A8, bf16 for BF16 */
+    /* Timing events of the shared expert's products, stamped like the
+     * routed ones above (on the stream the shared expert runs on: stream2
+     * when given, else `stream`); ignored without a shared expert. */
+    void* ev_sffn1_begin; /* start / end of the shared gate/up + SwiGLU */
+    void* ev_sffn1_end;
+    void* ev_sffn2_begin; /* start / end of the shared down projection */
+    void* ev_sffn2_end;
 } moe_aux;
 
 /* Workspace bytes an entry point needs for this descriptor (0 if none). */

@@ -770,6 +770,8 @@ moe_status moe_layer(const moe_desc* d, const moe_weights* w, const void* x, voi
     if (A.rows) L.rows = A.rows;
   }
 
+  const hipEvent_t s1b = static_cast<hipEvent_t>(A.ev_sffn1_begin), s1e = static_cast<hipEvent_t>(A.ev_sffn1_end);
+  const hipEvent_t s2b = static_cast<hipEvent_t>(A.ev_sffn2_begin), s2e = static_cast<hipEvent_t>(A.ev_sffn2_end);
   // The shared expert needs only x (and its int8 codes): it is forked onto
   // the caller's second stream, when one is given, before routing starts.
   const bool fork = d->T > 0 && d->shared_inter > 0 && A.stream2 && A.ev_fork && A.ev_join;
@@ -791,8 +793,8 @@ moe_status moe_layer(const moe_desc* d, const moe_weights* w, const void* x, voi
     }
     // (with the routed products apart, the shared down product is enqueued
     // later, after the small experts' down product)
-    st = run_ffn(d, shared_caps(shared_plan(d, w)), x, L.shared, L.shared_rows, rb, s2, nullptr, nullptr, nullptr,
-                 nullptr, PART_ALL, apart ? PART_NONE : PART_ALL);
+    st = run_ffn(d, shared_caps(shared_plan(d, w)), x, L.shared, L.shared_rows, rb, s2, s1b, s1e, s2b, s2e,
+                 PART_ALL, apart ? PART_NONE : PART_ALL);
     if (st != MOE_OK) return st;
   } else if (quant) {
     st = run_quant_x(d, x, L.routed, s);
@@ -821,8 +823,8 @@ moe_status moe_layer(const moe_desc* d, const moe_weights* w, const void* x, voi
     HIP_TRY(hipStreamWaitEvent(s2, static_cast<hipEvent_t>(A.ev_fork), 0));
     st = run_ffn(d, rp, x, L.routed, L.rows, rb, s2, nullptr, nullptr, nullptr, nullptr, PART_NONE, PART_SMALL);
     if (st != MOE_OK) return st;
-    st = run_ffn(d, shared_caps(shared_plan(d, w)), x, L.shared, L.shared_rows, rb, s2, nullptr, nullptr, nullptr,
-                 nullptr, PART_NONE, PART_ALL);
+    st = run_ffn(d, shared_caps(shared_plan(d, w)), x, L.shared, L.shared_rows, rb, s2, nullptr, nullptr, s2b, s2e,
+                 PART_NONE, PART_ALL);
     if (st != MOE_OK) return st;
   } else if (d->n_ffn > 0) {
     if (fork && quant) HIP_TRY(hipStreamWaitEvent(s, ev_join, 0));   // the codes of x
@@ -833,8 +835,7 @@ moe_status moe_layer(const moe_desc* d, const moe_weights* w, const void* x, voi
     HIP_TRY(hipEventRecord(ev_join, s2));   // after the shared expert (and small-expert down) on stream2
     HIP_TRY(hipStreamWaitEvent(s, ev_join, 0));
   } else if (d->shared_inter > 0) {
-    st = run_ffn(d, shared_caps(shared_plan(d, w)), x, L.shared, L.shared_rows, rb, s, nullptr, nullptr, nullptr,
-                 nullptr);
+    st = run_ffn(d, shared_caps(shared_plan(d, w)), x, L.shared, L.shared_rows, rb, s, s1b, s1e, s2b, s2e);
     if (st != MOE_OK) return st;
   }
   const CombineArgs cb = combine_args(d, x, L.rows, L.shared_rows, rb, idx, tw, offsets, slot_pos, y);

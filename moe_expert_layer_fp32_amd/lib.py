@@ -63,7 +63,8 @@ class MoeAux(ctypes.Structure):
                 ("slot_pos", _vp), ("q_x", _vp), ("s_x", _vp), ("ev_ffn1_begin", _vp), ("ev_ffn1_end", _vp),
                 ("ev_ffn2_begin", _vp), ("ev_ffn2_end", _vp), ("stream2", _vp), ("ev_fork", _vp),
                 ("ev_join", _vp), ("tuning", ctypes.POINTER(MoeTuning)), ("h", _vp), ("q_h", _vp), ("s_h", _vp),
-                ("rows", _vp)]
+                ("rows", _vp), ("ev_sffn1_begin", _vp), ("ev_sffn1_end", _vp), ("ev_sffn2_begin", _vp),
+                ("ev_sffn2_end", _vp)]
 
 
 _lib_handle = None
