@@ -377,6 +377,25 @@ moe_status moe_layer(const moe_desc* desc, const moe_weights* w, const void* x,
                      void* y, moe_aux* aux, void* ws, size_t ws_bytes,
                      void* stream);
 
+/*
+ * For callers that cannot allocate (code under stream capture that must not
+ * call hipMalloc, tight serving loops, hosts that forbid allocation): the
+ * whole layer with no workspace argument. The library keeps one device
+ * array of MOE_STATIC_WORKSPACE_BYTES per device (held until the process
+ * ends) and runs moe_layer with it; the call allocates and frees nothing.
+ * The device is the one current on the calling thread; `stream` must belong
+ * to it. The first call on a device looks up the array's address there.
+ * Arguments, results and errors are those of moe_layer, plus
+ * MOE_ERR_WORKSPACE when moe_workspace_bytes(desc, MOE_OP_LAYER) exceeds
+ * MOE_STATIC_WORKSPACE_BYTES (returned before any HIP call). The array is
+ * not cleared between calls (moe_layer needs no zeroed workspace). Every
+ * call on one device shares the one array: calls that overlap on a device
+ * (two host threads, or two streams at once) race; the caller orders them.
+ */
+#define MOE_STATIC_WORKSPACE_BYTES (64u << 20)
+moe_status moe_layer_static(const moe_desc* desc, const moe_weights* w, const void* x, void* y,
+                            moe_aux* aux, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

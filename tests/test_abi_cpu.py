@@ -202,3 +202,25 @@ def test_combine_requires_routing_tables_for_every_n_ffn(L, n_ffn):
     # with T == 0 every call is a no-op that reads nothing
     d.T = 0
     assert lib.moe_combine(ctypes.byref(d), None, None, None, None, None, None, None, None, None) == 0
+
+
+def test_layer_static_refuses_before_any_hip_call(L):
+    """moe_layer_static: a workspace need above MOE_STATIC_WORKSPACE_BYTES is
+    MOE_ERR_WORKSPACE and an invalid descriptor keeps moe_layer's status, both
+    returned on the host before any HIP call (none is possible here)."""
+    lib = L.load_library()
+    w = L.MoeWeights(router=FAKE, w13=FAKE, w2=FAKE, sw13=FAKE, sw2=FAKE)
+    big = _desc(L)                                    # the DeepSeek-style share needs ~360 MiB
+    assert L.moe_workspace_bytes(big, L.OP_LAYER) > L.STATIC_WORKSPACE_BYTES
+    assert lib.moe_layer_static(ctypes.byref(big), ctypes.byref(w), FAKE, FAKE, None, None) == -3
+    bad = _desc(L)
+    bad.k = 300
+    assert lib.moe_layer_static(ctypes.byref(bad), ctypes.byref(w), FAKE, FAKE, None, None) == -1
+    small = L.desc_from_config(get("longcat_zero_bf16"))
+    assert 0 < L.moe_workspace_bytes(small, L.OP_LAYER) <= L.STATIC_WORKSPACE_BYTES
+
+
+def test_static_workspace_size_matches_header(L):
+    text = open(os.path.join(ROOT, "include", "moe.h"), encoding="utf-8").read()
+    m = re.search(r"#define MOE_STATIC_WORKSPACE_BYTES \((\d+)u << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == L.STATIC_WORKSPACE_BYTES
