@@ -55,7 +55,9 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=10.0, help="target CPU time of the oracle sample")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-tune", action="store_true",
-                   help="skip choosing the shared expert's launch limits from measured runs (tuning.py)")
+                   help="skip choosing the launch limits from measured runs (tuning.py)")
+    p.add_argument("--limits", default="",
+                   help="JSON object of moe_tuning fields to use for every call instead of tuning")
     p.add_argument("--graph", action="store_true",
                    help="also time the same calls replayed from one captured HIP graph (graph_replay)")
     p.add_argument("--streams", type=int, default=2, choices=(1, 2),
@@ -358,7 +360,16 @@ def main() -> int:
     # Launch limits from measured runs (untimed): only the shared expert on
     # the second stream has candidates.
     tuned, t_struct = None, None
-    if second is not None and not args.no_tune:
+    if args.limits:
+        from moe_expert_layer_fp32_amd import tuning as TU
+        lim = TU.limits(**json.loads(args.limits))
+        t_struct = TU.to_struct(lim)
+        for a in auxes + ([warm_aux] if warm_aux is not None else []):
+            a.tuning = ctypes.pointer(t_struct)
+        if warm_aux is None:
+            warm_aux = L.MoeAux(tuning=ctypes.pointer(t_struct))
+        tuned = {"limits": lim, "source": "--limits"}
+    elif second is not None and not args.no_tune:
         from moe_expert_layer_fp32_amd import tuning as TU
         bucket = max(TU.load_bucket(c, cfg.ffn_begin, cfg.n_ffn) for c in counts_per_layer)
         key = TU.shape_key(desc, 2, bucket)

@@ -170,6 +170,26 @@ typedef struct moe_tuning {
     int32_t shared_ffn2_wgs;  /* shared expert, down projection */
     int32_t routed_ffn1_wgs;  /* routed experts, gate/up projection + SwiGLU */
     int32_t routed_ffn2_wgs;  /* routed experts, down projection */
+    /* Tile choice per expert load: SwiftGMM's switch between streaming an
+     * expert's weights (GEMV mode) and tiled products (GEMM mode) by how many
+     * tokens the expert received (same page and section). 0 leaves the
+     * library's default; each choice changes only which kernel computes a
+     * product (fp32 summation order), never the workspace size.
+     *  - prefill_tokens: from this many tokens up (default 1024) the routed
+     *    experts are classed by their row count as below; with fewer, every
+     *    expert takes 64-row tiles in one launch (the reduction split over
+     *    workgroups when the experts alone are too few).
+     *  - stream_max_rows (theta): experts with at most this many rows stream
+     *    their weights through 64-row tiles (default 64); larger experts take
+     *    128-row tiles, or 256-row tiles from big_min_rows.
+     *  - big_min_rows: bf16 experts with at least this many rows take the
+     *    256-row tiles (default 256).
+     *  - dense_big_rows: bf16 dense products (the shared expert) of at least
+     *    this many rows take the 256-row tiles (default 2048). */
+    int32_t prefill_tokens;
+    int32_t stream_max_rows;
+    int32_t big_min_rows;
+    int32_t dense_big_rows;
 } moe_tuning;
 
 /*

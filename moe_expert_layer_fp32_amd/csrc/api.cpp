@@ -71,9 +71,34 @@ constexpr int PERSISTENT_WGS = 512;   // grid cap of the tiled kernel (it loops 
 // m-tiles (LdsArgs::group_m). Measured on the prefill shared expert (8192
 // rows, one stream): gate/up 474 -> 457 us, down 296 -> 274 us.
 constexpr int DENSE_GROUP_M = 8;
+// Tile choice defaults (moe_tuning's prefill_tokens, stream_max_rows,
+// big_min_rows, dense_big_rows; see moe.h). 256-row tiles: panels of 4
+// m-tiles for dense products (4 x 8 tiles of an XCD's 32 compute units run
+// together), m-tile fastest for routed experts.
+constexpr int STREAM_MAX_ROWS = 64;
+constexpr int BIG_MIN_ROWS = 256;
+constexpr int DENSE_BIG_ROWS = 2048;
+constexpr int BIG_GROUP_M = 4;
+constexpr int BIG_WGS = 256;          // one 256-row workgroup per compute unit (128 KiB of LDS)
+
+struct TilePolicy {
+  int prefill_tokens = PREFILL_T;
+  int stream_max_rows = STREAM_MAX_ROWS;
+  int big_min_rows = BIG_MIN_ROWS;
+  int dense_big_rows = DENSE_BIG_ROWS;
+};
+TilePolicy policy_of(const moe_tuning& t) {
+  TilePolicy p;
+  if (t.prefill_tokens > 0) p.prefill_tokens = t.prefill_tokens;
+  if (t.stream_max_rows > 0) p.stream_max_rows = t.stream_max_rows;
+  if (t.big_min_rows > 0) p.big_min_rows = t.big_min_rows;
+  if (t.dense_big_rows > 0) p.dense_big_rows = t.dense_big_rows;
+  return p;
+}
 
 struct DensePlan {
   bool lds;
+  bool big = false;   // 256-row tiles (gemm_big): no reduction split
   LdsArgs L;
   int tiles_y;
   int tile_rows;
@@ -82,10 +107,29 @@ struct DensePlan {
 
 // cap > 0: at most that many workgroups (a caller's launch limit); it only
 // lowers the split target and the persistent grid, so the plan never needs
-// more split-K workspace than the uncapped one.
-DensePlan plan_dense(int M, int N, int K, GemmElem el, int nacc, int cap = 0) {
+// more split-K workspace than the uncapped one. With a policy, bf16 products
+// of planes 1 (sum) or 2 (SwiGLU) and at least dense_big_rows rows take the
+// 256-row tiles, which need no workspace; without one (workspace sizing) the
+// plan is the 64/128-row one, whose split-K partial sums bound every plan's.
+DensePlan plan_dense(int M, int N, int K, GemmElem el, int nacc, int cap = 0, const TilePolicy* pol = nullptr,
+                     int planes = 0) {
   const int target = cap > 0 ? std::min(cap, TARGET_WGS) : TARGET_WGS;
   DensePlan p{};
+  const GemmEpi epi = nacc == 2 ? EPI_SWIGLU : EPI_SUM;
+  if (pol && el == ELEM_BF16 && planes == nacc && M >= pol->dense_big_rows && gemm_big_fits(N, K, epi)) {
+    p.lds = true;
+    p.big = true;
+    LdsArgs& L = p.L;
+    L.tile_rows = BIG_TILE_ROWS;
+    L.splits = 1;
+    L.min_rows = 0;
+    L.max_rows = INT32_MAX;
+    L.part_rows = M;
+    L.max_wgs = cap > 0 ? std::min(cap, BIG_WGS) : BIG_WGS;
+    L.group_m = BIG_GROUP_M;
+    p.tiles_y = ceil_div(M, BIG_TILE_ROWS);
+    return p;
+  }
   const int ch = lds_chunk_elems(el);
   if (M <= 64 || K % ch != 0 || N % 32 != 0) {
     p.lds = false;
@@ -273,13 +317,17 @@ LayerWs carve_layer(Carve& c, const moe_desc* d) {
 // ---------------------------------------------------------------------------
 // Launch one dense product with its plan (tiled LDS GEMM or streaming).
 moe_status run_dense(GemmArgs g, int M, GemmElem el, int planes, GemmEpi epi, void* partial, hipStream_t s,
-                     KernelEvents ev = {}, int cap = 0) {
+                     KernelEvents ev, int cap, const TilePolicy& pol) {
   const int nacc = epi == EPI_SWIGLU ? 2 : 1;
-  const DensePlan p = plan_dense(M, g.N, g.K, el, nacc, cap);
+  const DensePlan p = plan_dense(M, g.N, g.K, el, nacc, cap, &pol, planes);
   if (p.partial_bytes > plan_dense(M, g.N, g.K, el, nacc).partial_bytes) return MOE_ERR_INVALID_ARG;
   g.offsets = nullptr;
   g.dense_rows = M;
   g.tiles_y = p.tiles_y;
+  if (p.big) {
+    HIP_TRY(launch_gemm_big(g, p.L, epi, s, ev));
+    return MOE_OK;
+  }
   if (!p.lds) {
     g.dense_tile_rows = p.tile_rows;
     g.ksplit = gemm_stream_ksplit(g.N / 16, g.K / kf_of(el));
@@ -311,15 +359,18 @@ enum RoutedPart { PART_NONE = 0, PART_SMALL = 1, PART_LARGE = 2, PART_ALL = 3 };
 // Whether moe_layer may place the two prefill launches of a routed product on
 // different streams: bf16 / fp32 (the W8A8 row quantisation between the
 // products covers every expert at once) and both products tiled unsplit.
-bool routed_parts_apart(const moe_desc* d) {
-  return d->T >= PREFILL_T && !w8a8(d) && d->n_ffn > 0 && routed_tiled(d, d->inter, d->d) &&
+bool routed_parts_apart(const moe_desc* d, const TilePolicy& pol) {
+  return d->T >= pol.prefill_tokens && !w8a8(d) && d->n_ffn > 0 && routed_tiled(d, d->inter, d->d) &&
          routed_tiled(d, d->d, d->inter);
 }
 
 moe_status run_routed(GemmArgs g, const moe_desc* d, GemmElem el, int planes, GemmEpi epi, void* partial,
-                      hipStream_t s, KernelEvents ev = {}, int cap = 0, int part = PART_ALL) {
+                      hipStream_t s, KernelEvents ev, int cap, int part, const TilePolicy& pol) {
   if (part == PART_NONE) return MOE_OK;
-  const int splits = routed_splits(d, g.N, g.K);
+  const bool prefill = d->T >= pol.prefill_tokens;
+  // the reduction is split only at the default decode sizes (the workspace
+  // holds the partial sums for exactly those)
+  const int splits = prefill ? 1 : routed_splits(d, g.N, g.K);
   if (splits > 1) {
     LdsArgs L{};
     L.wave_features = 32;
@@ -335,7 +386,7 @@ moe_status run_routed(GemmArgs g, const moe_desc* d, GemmElem el, int planes, Ge
     return MOE_OK;
   }
   const long tiled_wgs = long(g.n_groups) * ceil_div(g.N, 128);
-  if (routed_tiled(d, g.N, g.K) && (tiled_wgs >= TARGET_WGS || d->T >= PREFILL_T)) {
+  if (routed_tiled(d, g.N, g.K) && (tiled_wgs >= TARGET_WGS || prefill)) {
     LdsArgs L{};
     L.wave_features = 32;
     L.splits = 1;
@@ -343,26 +394,60 @@ moe_status run_routed(GemmArgs g, const moe_desc* d, GemmElem el, int planes, Ge
     L.max_wgs = capped_wgs(cap, 1);
     L.tile_rows = 64;
     L.min_rows = 1;
-    L.max_rows = d->T >= PREFILL_T ? 64 : INT32_MAX;
-    // with at most 64 rows an expert has one 64-row tile
-    g.tiles_y = d->T >= PREFILL_T ? g.n_groups : ceil_div(r_max(d), L.tile_rows) + g.n_groups;
-    if (d->T < PREFILL_T) {
+    L.max_rows = INT32_MAX;
+    g.tiles_y = ceil_div(r_max(d), L.tile_rows) + g.n_groups;
+    if (!prefill) {
       HIP_TRY(launch_gemm_lds(g, L, el, planes, epi, s, ev));
       return MOE_OK;
     }
-    if (part & PART_SMALL)
-      HIP_TRY(launch_gemm_lds(g, L, el, planes, epi, s,
-                              part == PART_SMALL ? ev : KernelEvents{ev.start, nullptr}));
+    // Prefill: experts classed by row count (the per-expert mode switch;
+    // which expert is in which class is decided on the device from the
+    // offsets). Streaming class: at most theta rows, 64-row tiles; middle
+    // class: 128-row tiles; large class: 256-row tiles (bf16 shapes that fit
+    // them). PART_SMALL is the streaming class, PART_LARGE the other two.
+    const int theta = pol.stream_max_rows;
+    const bool big = el == ELEM_BF16 && planes == (epi == EPI_SWIGLU ? 2 : 1) && gemm_big_fits(g.N, g.K, epi) &&
+                     pol.big_min_rows <= r_max(d);
+    const int big_lo = big ? std::max(theta + 1, pol.big_min_rows) : INT32_MAX;
+    const bool has_mid = theta + 1 < big_lo;
+    // launches in order: [small], [mid], [big]; the events go on the first
+    // and last launch made by this call
+    const int n_launch = ((part & PART_SMALL) ? 1 : 0) + ((part & PART_LARGE) ? int(has_mid) + int(big) : 0);
+    int k_launch = 0;
+    auto events = [&]() {
+      KernelEvents e{k_launch == 0 ? ev.start : nullptr, k_launch == n_launch - 1 ? ev.stop : nullptr};
+      ++k_launch;
+      return e;
+    };
+    if (part & PART_SMALL) {
+      L.max_rows = theta;
+      // with at most 64 rows an expert has one 64-row tile
+      g.tiles_y = theta <= 64 ? g.n_groups : ceil_div(r_max(d), L.tile_rows) + g.n_groups;
+      HIP_TRY(launch_gemm_lds(g, L, el, planes, epi, s, events()));
+    }
     if (!(part & PART_LARGE)) return MOE_OK;
-    // experts with more rows: 128-row tiles, 64 features per wavefront for
-    // one-plane products (twice the matrix-core work per weight fragment)
-    L.tile_rows = 128;
-    L.min_rows = 65;
-    L.max_rows = INT32_MAX;
-    L.wave_features = planes == 1 && g.N % 256 == 0 ? 64 : 32;
-    g.tiles_y = ceil_div(r_max(d), L.tile_rows) + g.n_groups;
-    HIP_TRY(launch_gemm_lds(g, L, el, planes, epi, s,
-                            part == PART_LARGE ? ev : KernelEvents{nullptr, ev.stop}));
+    if (has_mid) {
+      // 128-row tiles, 64 features per wavefront for one-plane products
+      // (twice the matrix-core work per weight fragment)
+      L.tile_rows = 128;
+      L.min_rows = theta + 1;
+      L.max_rows = big_lo - 1;
+      L.wave_features = planes == 1 && g.N % 256 == 0 ? 64 : 32;
+      g.tiles_y = ceil_div(r_max(d), L.tile_rows) + g.n_groups;
+      HIP_TRY(launch_gemm_lds(g, L, el, planes, epi, s, events()));
+    }
+    if (big) {
+      LdsArgs B{};
+      B.tile_rows = BIG_TILE_ROWS;
+      B.splits = 1;
+      B.min_rows = big_lo;
+      B.max_rows = INT32_MAX;
+      B.part_rows = r_max(d);
+      B.max_wgs = cap > 0 ? std::min(cap, BIG_WGS) : BIG_WGS;
+      B.group_m = 1;
+      g.tiles_y = ceil_div(r_max(d), BIG_TILE_ROWS) + g.n_groups;
+      HIP_TRY(launch_gemm_big(g, B, epi, s, events()));
+    }
     return MOE_OK;
   }
   g.max_group_rows = 0;
@@ -449,11 +534,13 @@ struct FfnPlan {
   const int32_t* sorted_slot;  // routed only
   int rows_bound;              // routed: r_max; shared: T
   int cap1 = 0, cap2 = 0;      // workgroup caps of the two products (0: none)
+  TilePolicy pol{};            // tile choice (library defaults unless tuned)
 };
 // The plan with the caller's launch limits for these products applied.
-FfnPlan with_caps(FfnPlan p, int cap1, int cap2) {
+FfnPlan with_caps(FfnPlan p, int cap1, int cap2, const TilePolicy& pol) {
   p.cap1 = cap1;
   p.cap2 = cap2;
+  p.pol = pol;
   return p;
 }
 
@@ -494,8 +581,8 @@ moe_status run_ffn(const moe_desc* d, const FfnPlan& p, const void* x, const Ffn
   g1.out_bf16 = d->dtype == MOE_DTYPE_BF16;
   const KernelEvents ev1{e1b, e1e}, ev2{e2b, e2e};
   if (part1 != PART_NONE) {
-    st = routed ? run_routed(g1, d, el, 2, EPI_SWIGLU, f.partial, s, ev1, p.cap1, part1)
-                : run_dense(g1, d->T, el, 2, EPI_SWIGLU, f.partial, s, ev1, p.cap1);
+    st = routed ? run_routed(g1, d, el, 2, EPI_SWIGLU, f.partial, s, ev1, p.cap1, part1, p.pol)
+                : run_dense(g1, d->T, el, 2, EPI_SWIGLU, f.partial, s, ev1, p.cap1, p.pol);
     if (st != MOE_OK) return st;
   }
 
@@ -522,8 +609,8 @@ moe_status run_ffn(const moe_desc* d, const FfnPlan& p, const void* x, const Ffn
   g2.ldo = size_t(d->d) * (rows_bf16 ? 2 : 4);
   g2.out_bf16 = rows_bf16;
   if (part2 != PART_NONE) {
-    st = routed ? run_routed(g2, d, el, 1, EPI_SUM, f.partial, s, ev2, p.cap2, part2)
-                : run_dense(g2, d->T, el, 1, EPI_SUM, f.partial, s, ev2, p.cap2);
+    st = routed ? run_routed(g2, d, el, 1, EPI_SUM, f.partial, s, ev2, p.cap2, part2, p.pol)
+                : run_dense(g2, d->T, el, 1, EPI_SUM, f.partial, s, ev2, p.cap2, p.pol);
     if (st != MOE_OK) return st;
   }
   return MOE_OK;
@@ -741,7 +828,8 @@ moe_status moe_layer(const moe_desc* d, const moe_weights* w, const void* x, voi
     if (given != 0 && given != 3) return MOE_ERR_INVALID_ARG;
     if (aux->stream2 && aux->stream2 == stream) return MOE_ERR_INVALID_ARG;
     const moe_tuning* t = aux->tuning;
-    if (t && (t->shared_ffn1_wgs < 0 || t->shared_ffn2_wgs < 0 || t->routed_ffn1_wgs < 0 || t->routed_ffn2_wgs < 0))
+    if (t && (t->shared_ffn1_wgs < 0 || t->shared_ffn2_wgs < 0 || t->routed_ffn1_wgs < 0 || t->routed_ffn2_wgs < 0 ||
+              t->prefill_tokens < 0 || t->stream_max_rows < 0 || t->big_min_rows < 0 || t->dense_big_rows < 0))
       return MOE_ERR_INVALID_ARG;
   }
   const size_t need = ws_bytes_of(d, MOE_OP_LAYER);
@@ -759,8 +847,9 @@ moe_status moe_layer(const moe_desc* d, const moe_weights* w, const void* x, voi
   int32_t* sorted_slot = A.sorted_slot ? A.sorted_slot : L.sorted_slot;
   int32_t* slot_pos = A.slot_pos ? A.slot_pos : L.slot_pos;
   const moe_tuning tune = A.tuning ? *A.tuning : moe_tuning{};
-  auto shared_caps = [&](const FfnPlan& p) { return with_caps(p, tune.shared_ffn1_wgs, tune.shared_ffn2_wgs); };
-  auto routed_caps = [&](const FfnPlan& p) { return with_caps(p, tune.routed_ffn1_wgs, tune.routed_ffn2_wgs); };
+  const TilePolicy pol = policy_of(tune);
+  auto shared_caps = [&](const FfnPlan& p) { return with_caps(p, tune.shared_ffn1_wgs, tune.shared_ffn2_wgs, pol); };
+  auto routed_caps = [&](const FfnPlan& p) { return with_caps(p, tune.routed_ffn1_wgs, tune.routed_ffn2_wgs, pol); };
   if (A.q_x) L.routed.qx = L.shared.qx = A.q_x;
   if (A.s_x) L.routed.sx = L.shared.sx = A.s_x;
   if (d->n_ffn > 0) {
@@ -776,7 +865,7 @@ moe_status moe_layer(const moe_desc* d, const moe_weights* w, const void* x, voi
   // the caller's second stream, when one is given, before routing starts.
   const bool fork = d->T > 0 && d->shared_inter > 0 && A.stream2 && A.ev_fork && A.ev_join;
   const bool quant = d->T > 0 && w8a8(d);
-  const bool apart = fork && routed_parts_apart(d);
+  const bool apart = fork && routed_parts_apart(d, pol);
   hipStream_t s2 = static_cast<hipStream_t>(A.stream2);
   hipEvent_t ev_join = static_cast<hipEvent_t>(A.ev_join);
   if (fork) {

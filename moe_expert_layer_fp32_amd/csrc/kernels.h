@@ -94,6 +94,17 @@ struct LdsArgs {
 hipError_t launch_gemm_lds(const GemmArgs& a, const LdsArgs& L, GemmElem elem, int planes, GemmEpi epi,
                            hipStream_t stream, KernelEvents ev = {});
 int lds_chunk_elems(GemmElem elem);
+
+// Large-tile bf16 GEMM (gemm_big.hip): 256 rows x 256 weight columns per
+// tile, both operands staged in LDS by direct-to-LDS loads, one workgroup per
+// compute unit. Same GemmArgs (grouped or dense rows) and LdsArgs (row-count
+// class, persistent grid cap, panel order); no reduction split, no scales or
+// bias (bf16 SwiGLU gate/up or one-plane products). Fits when K % 64 == 0 and
+// N % 128 (SwiGLU) or N % 256 (one plane) == 0. tiles_y: m-tiles of 256 rows.
+constexpr int BIG_TILE_ROWS = 256;
+bool gemm_big_fits(int N, int K, GemmEpi epi);
+hipError_t launch_gemm_big(const GemmArgs& a, const LdsArgs& L, GemmEpi epi, hipStream_t stream,
+                           KernelEvents ev = {});
 // Reduce pass of a split product: partial sums added in split order, then
 // the product's epilogue (stop: optional timing event stamped at its end).
 hipError_t launch_gemm_reduce(const GemmArgs& a, const LdsArgs& L, GemmElem elem, GemmEpi epi, hipStream_t stream,

@@ -27,15 +27,18 @@ import numpy as np
 
 from . import lib as L
 
-FIELDS = ("shared_ffn1_wgs", "shared_ffn2_wgs", "routed_ffn1_wgs", "routed_ffn2_wgs")
+FIELDS = ("shared_ffn1_wgs", "shared_ffn2_wgs", "routed_ffn1_wgs", "routed_ffn2_wgs",
+          "prefill_tokens", "stream_max_rows", "big_min_rows", "dense_big_rows")
 
 # Candidate caps (shared gate/up, shared down); the routed launches keep the
 # library's grids. (0, 0) is the library's own choice and always a candidate.
 SHARED_CANDIDATES = ((0, 0), (96, 0), (128, 0), (192, 0), (128, 128), (192, 192))
 
 
-def limits(shared_ffn1_wgs=0, shared_ffn2_wgs=0, routed_ffn1_wgs=0, routed_ffn2_wgs=0) -> dict:
-    return dict(zip(FIELDS, (shared_ffn1_wgs, shared_ffn2_wgs, routed_ffn1_wgs, routed_ffn2_wgs)))
+def limits(shared_ffn1_wgs=0, shared_ffn2_wgs=0, routed_ffn1_wgs=0, routed_ffn2_wgs=0, prefill_tokens=0,
+           stream_max_rows=0, big_min_rows=0, dense_big_rows=0) -> dict:
+    return dict(zip(FIELDS, (shared_ffn1_wgs, shared_ffn2_wgs, routed_ffn1_wgs, routed_ffn2_wgs, prefill_tokens,
+                             stream_max_rows, big_min_rows, dense_big_rows)))
 
 
 def label(lim: dict) -> str:

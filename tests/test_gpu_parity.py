@@ -346,6 +346,73 @@ def test_grouped_ffn_tile_boundaries(T, dtype):
     assert beyond_flips <= U.TOL[dtype], f"rows error {beyond_flips}"
 
 
+# rows per resident expert around the 256-row tiles of the prefill regime:
+# empty, streaming (<= 64), 128-row tiles (65 .. 255), one 256-row tile
+# (256), a ragged second one (257), and two or three 256-row tiles
+BIG_COUNTS = (0, 1, 64, 65, 255, 256, 257, 511, 512, 513)
+
+
+@pytest.mark.parametrize("inter", [128, 256])
+def test_grouped_ffn_big_tile_boundaries(inter):
+    """Prefill regime (2900 tokens, bf16): resident experts with 0, 1, 64,
+    65, 255, 256, 257, 511, 512 and 513 rows, so every row-count class runs
+    (64-row streaming tiles, 128-row tiles, 256-row tiles with full and
+    ragged last tiles); every row against the oracle, plus the shared expert
+    over all 2900 tokens in 256-row tiles (a ragged last m-tile)."""
+    L, DeviceLayer, to_device = _L()
+    T = 2900
+    cfg = MoEConfig(name="bigtiles", T=T, d=256, E=16, k=1, gate="softmax", n_ffn=10, inter=inter,
+                    shared_inter=256, dtype="bf16")
+    inp = make_inputs(cfg, seed=8)
+    lay = DeviceLayer(cfg, inp)
+    g = np.random.default_rng(23)
+    ids = np.concatenate([np.full(c, e, np.int32) for e, c in enumerate(BIG_COUNTS)])
+    rest = g.integers(10, 16, size=T - ids.size).astype(np.int32)
+    idx = g.permutation(np.concatenate([ids, rest])).reshape(T, 1).astype(np.int32)
+    U.say(f"[gpu] big tile boundaries T={T} inter={inter} counts={BIG_COUNTS}")
+    counts, offsets, ss, sp = lay.permute(torch.from_numpy(idx).cuda())
+    rows = lay.grouped_ffn(L.FFN_ROUTED, offsets, ss)
+    shared = lay.grouped_ffn(L.FFN_SHARED)
+    torch.cuda.synchronize()
+    assert U.np_of(counts)[:10].tolist() == list(BIG_COUNTS)
+    want, _ = _expected_rows(cfg, inp, idx, O.routing_tables(idx, cfg.E))
+    got = U.np_of(rows)[: want.shape[0]]
+    lit, _ = U.output_errors(got, want, "f32")
+    U.record(test="grouped_ffn_big_tile_boundaries", inter=inter, err_rows_literal=lit)
+    assert lit <= U.TOL["bf16"], f"routed rows error {lit}"
+    want_s = O.shared_ffn(inp, cfg, np.asarray(O.x_f32(inp), np.float32))
+    lit_s, _ = U.output_errors(U.np_of(shared), want_s, "f32")
+    U.record(test="grouped_ffn_big_tile_boundaries_shared", inter=inter, err_rows_literal=lit_s)
+    assert lit_s <= U.TOL["bf16"], f"shared rows error {lit_s}"
+
+
+@pytest.mark.parametrize("policy", [
+    dict(prefill_tokens=256, stream_max_rows=100, big_min_rows=300, dense_big_rows=512),
+    dict(prefill_tokens=256, stream_max_rows=16, big_min_rows=64, dense_big_rows=256),
+    dict(prefill_tokens=4096),                       # the decode regime at 1500 tokens
+])
+def test_layer_tile_policy(policy):
+    """moe_layer under non-default tile choices (moe_tuning: the prefill
+    threshold, theta of the weight-streaming class, the 256-row class of
+    experts and of dense products), one and two streams, against the
+    oracle; the routing tables are those of the default call."""
+    L, DeviceLayer, to_device = _L()
+    from moe_expert_layer_fp32_amd.layer import SecondStream
+    cfg = MoEConfig(name="policy", T=1500, d=512, E=32, k=4, gate="sigmoid", n_ffn=20, inter=256,
+                    shared_inter=256, dtype="bf16", bias=("zipf", 1.1))
+    inp = make_inputs(cfg, seed=4)
+    lay = DeviceLayer(cfg, inp)
+    t = L.MoeTuning(**policy)
+    U.say(f"[gpu] layer tile policy {policy}")
+    y = _check_layer(cfg, inp, lay, tuning=t)
+    y2 = _check_layer(cfg, inp, lay, second=SecondStream(), tuning=t)
+    y0 = lay.layer()
+    torch.cuda.synchronize()
+    _, dev = U.output_errors(U.np_of(y), U.np_of(y0).astype(np.float64), cfg.dtype)
+    U.record(test="layer_tile_policy", policy=policy, err_vs_default=dev)
+    assert torch.equal(_bits(y), _bits(y2))
+
+
 @pytest.mark.parametrize("name", ["longcat_zero_bf16", "pangu_moge_w8a8"])
 def test_layer_writes_nothing_outside_its_buffers(name):
     """Guard bands around y and every moe_aux output buffer (filled with a

@@ -43,7 +43,7 @@ def test_library_choice_is_no_struct(TU):
     assert TU.to_struct(TU.limits()) is None
     t = TU.to_struct(TU.limits(96, 0, 8, 0))
     assert (t.shared_ffn1_wgs, t.shared_ffn2_wgs, t.routed_ffn1_wgs, t.routed_ffn2_wgs) == (96, 0, 8, 0)
-    assert TU.label(TU.limits(96, 0, 8, 0)) == "96/0/8/0"
+    assert TU.label(TU.limits(96, 0, 8, 0)) == "96/0/8/0/0/0/0/0"
 
 
 def test_load_bucket_and_key(TU):
