@@ -58,6 +58,10 @@ def parse():
                    help="skip choosing the launch limits from measured runs (tuning.py)")
     p.add_argument("--limits", default="",
                    help="JSON object of moe_tuning fields to use for every call instead of tuning")
+    p.add_argument("--tune", action="store_true",
+                   help="time the candidate limits even when the shipped table has an entry for this shape")
+    p.add_argument("--save-tuning", default="",
+                   help="merge the entry tuned by this run into the JSON table at this path")
     p.add_argument("--graph", action="store_true",
                    help="also time the same calls replayed from one captured HIP graph (graph_replay)")
     p.add_argument("--streams", type=int, default=2, choices=(1, 2),
@@ -369,25 +373,40 @@ def main() -> int:
         if warm_aux is None:
             warm_aux = L.MoeAux(tuning=ctypes.pointer(t_struct))
         tuned = {"limits": lim, "source": "--limits"}
-    elif second is not None and not args.no_tune:
+    elif not args.no_tune:
+        # The tiling table: the shipped entry for this shape, stream count and
+        # load bucket, else limits timed now on these calls (untimed region).
         from moe_expert_layer_fp32_amd import tuning as TU
+        streams = 2 if second is not None else 1
         bucket = max(TU.load_bucket(c, cfg.ffn_begin, cfg.n_ffn) for c in counts_per_layer)
-        key = TU.shape_key(desc, 2, bucket)
-        cache = TU.TilingCache()
-        tune_aux = second.fill(L.MoeAux())
+        key = TU.shape_key(desc, streams, bucket)
+        cache = TU.TilingCache.shipped()
+        lim = None if args.tune else cache.lookup(key)
+        source = "shipped table"
+        if lim is None:
+            source = "tuned in this run"
+            tune_aux = second.fill(L.MoeAux()) if second is not None else L.MoeAux()
 
-        def run(t, i):
-            tune_aux.tuning = ctypes.pointer(t) if t is not None else None
-            lay = layers[i % n_layers]
-            L.moe_layer(desc, lay.weights, lay.x, y, tune_aux, ws)
+            def run(t, i):
+                tune_aux.tuning = ctypes.pointer(t) if t is not None else None
+                lay = layers[i % n_layers]
+                L.moe_layer(desc, lay.weights, lay.x, y, tune_aux, ws)
 
-        lim = cache.tune(key, run, torch.cuda.synchronize, calls=max(5, min(20, 4000 // max(1, cfg.T))))
+            fresh = TU.TilingCache()
+            lim = fresh.tune(key, run, torch.cuda.synchronize, candidates=TU.candidates_for(desc, streams),
+                             calls=max(5, min(20, 4000 // max(1, cfg.T))))
+            cache.table[key] = fresh.table[key]
+            if args.save_tuning:
+                fresh.merge_into(args.save_tuning)
         t_struct = TU.to_struct(lim)
         if t_struct is not None:
-            for a in auxes + [warm_aux]:
+            for a in auxes:
                 a.tuning = ctypes.pointer(t_struct)
-        tuned = {"limits": lim, "candidates_us": cache.table[key]["us"], "candidate_order": "/".join(TU.FIELDS),
-                 "load_bucket": bucket}
+            if warm_aux is None:
+                warm_aux = L.MoeAux()
+            warm_aux.tuning = ctypes.pointer(t_struct)
+        tuned = {"limits": lim, "source": source, "key": key, "candidates_us": cache.table[key].get("us"),
+                 "candidate_order": "/".join(TU.FIELDS), "load_bucket": bucket}
 
     for i in range(W):
         lay = layers[i % n_layers]

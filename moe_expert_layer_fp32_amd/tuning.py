@@ -1,25 +1,31 @@
-"""Launch limits for moe_layer chosen from measured runs.
+"""Launch limits and tile choices for moe_layer chosen from measured runs.
 
 This is the history-based tiling cache of SwiftGMM (page "华为技术披露集
 VOL.12：昇腾×盘古", section SwiftGMM：专家计算突击队，闪电速度抵达推理算力战场):
 tile parameters are predicted from past loads instead of being fixed. Here
-the parameters are the workgroup caps of moe_tuning. For one layer shape and
-one bucket of its per-expert token counts, a few candidate caps are timed on
-the caller's own layer calls, and the fastest is kept in a host-side table.
-The table is keyed by plain values and can be saved to JSON and loaded back.
-A serving loop takes the bucket from the counts of its previous call
-(moe_aux.counts), so choosing an entry never waits for the device.
+the parameters are the members of moe_tuning: the tile choice by per-expert
+row count (the prefill threshold, theta of the weight-streaming class, the
+256-row classes of experts and of dense products) and the workgroup caps of
+each product. For one layer shape, stream count and bucket of its
+per-expert token counts, a few candidates are timed on the caller's own
+layer calls and the fastest is kept in a host-side table. The table is keyed
+by plain values and saved to JSON; the package ships one measured on an
+MI355X for the workloads of this repository (tuning_table.json), which
+callers load instead of tuning from empty. A serving loop takes the bucket
+from the counts of its previous call (moe_aux.counts), so choosing an entry
+never waits for the device.
 
-The caps matter where the shared expert runs on a second stream: its
-persistent GEMMs can occupy every compute unit while the router, gate and
-permutation of the same call wait for room. Capping it leaves units free
-for them. Whether that pays depends on the shape, so it is measured rather
-than modelled.
+The caps matter where the shared expert runs on a second stream: persistent
+GEMMs can occupy every compute unit while the other stream's products wait
+for room, and a product whose tiles do not fill the last round of compute
+units leaves room the other stream can use. Whether that pays depends on the
+shape, so it is measured rather than modelled.
 """
 from __future__ import annotations
 
 import json
 import math
+import os
 import time
 from typing import Callable
 
@@ -27,12 +33,38 @@ import numpy as np
 
 from . import lib as L
 
+TABLE_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "tuning_table.json")
+
 FIELDS = ("shared_ffn1_wgs", "shared_ffn2_wgs", "routed_ffn1_wgs", "routed_ffn2_wgs",
           "prefill_tokens", "stream_max_rows", "big_min_rows", "dense_big_rows")
 
-# Candidate caps (shared gate/up, shared down); the routed launches keep the
-# library's grids. (0, 0) is the library's own choice and always a candidate.
+# Candidate caps (shared gate/up, shared down); (0, 0) is the library's own
+# choice and always a candidate.
 SHARED_CANDIDATES = ((0, 0), (96, 0), (128, 0), (192, 0), (128, 128), (192, 192))
+NO_BIG = 1 << 30          # a big_min_rows / dense_big_rows no layer reaches: 256-row tiles off
+
+
+def candidates_for(desc: L.MoeDesc, streams: int) -> list[dict]:
+    """Candidate limits for one layer shape. Decode sizes (below the default
+    prefill threshold of 1024 tokens): the shared expert's caps, and the
+    per-expert tile classes of the prefill regime applied early. Prefill
+    sizes: caps of the shared products and of the routed gate/up, with and
+    without 256-row tiles for routed experts."""
+    out = []
+    has_shared = desc.shared_inter > 0
+    if desc.T < 1024:
+        shared = SHARED_CANDIDATES if (has_shared and streams == 2) else ((0, 0),)
+        for c in shared:
+            out.append(limits(*c))
+        out.append(limits(prefill_tokens=max(1, desc.T)))
+        return out
+    shared = ((0, 0), (128, 128), (192, 192)) if (has_shared and streams == 2) else ((0, 0),)
+    routed = ((0, 0), (160, 0)) if streams == 2 else ((0, 0),)
+    for big in (0, NO_BIG):
+        for sc in shared:
+            for rc in routed:
+                out.append(limits(sc[0], sc[1], rc[0], rc[1], big_min_rows=big))
+    return out
 
 
 def limits(shared_ffn1_wgs=0, shared_ffn2_wgs=0, routed_ffn1_wgs=0, routed_ffn2_wgs=0, prefill_tokens=0,
@@ -81,12 +113,14 @@ class TilingCache:
     def tune(self, key: str, run: Callable[[L.MoeTuning | None, int], None], sync: Callable[[], None],
              candidates=SHARED_CANDIDATES, calls: int = 20, reps: int = 3,
              clock: Callable[[], float] = time.perf_counter) -> dict:
-        """Time every candidate and keep the fastest for `key`. run(tuning, i)
+        """Time every candidate and keep the fastest for `key`. Candidates are
+        limits dicts or tuples of the leading fields. run(tuning, i)
         enqueues the i-th layer call with that moe_tuning; sync() waits for the
         device. Each candidate's time is the best over `reps` rounds of
         `calls` calls (the calls are device-bound, so wall time between two
         synchronisations is device time). clock: seconds, monotonic."""
-        cands = {label(lim): lim for lim in (limits(*c) for c in candidates)}
+        as_dict = [c if isinstance(c, dict) else limits(*c) for c in candidates]
+        cands = {label(lim): lim for lim in as_dict}
         times: dict[str, float] = {}
         for _ in range(reps):
             for name, lim in cands.items():
@@ -112,3 +146,14 @@ class TilingCache:
     def load(cls, path: str) -> "TilingCache":
         with open(path) as f:
             return cls(json.load(f))
+
+    @classmethod
+    def shipped(cls) -> "TilingCache":
+        """The table measured for this repository's workloads (empty if absent)."""
+        return cls.load(TABLE_PATH) if os.path.exists(TABLE_PATH) else cls()
+
+    def merge_into(self, path: str) -> None:
+        """Add this table's entries to the JSON table at `path` (created if absent)."""
+        old = TilingCache.load(path).table if os.path.exists(path) else {}
+        old.update(self.table)
+        TilingCache(old).save(path)

@@ -57,3 +57,40 @@ def test_load_bucket_and_key(TU):
     k1, k2 = TU.shape_key(d, 2, 5), TU.shape_key(d, 2, 6)
     assert k1 != k2 and "T=512" in k1 and "streams=2" in k1
     assert TU.shape_key(L.MoeDesc(T=256, d=7168, E=256, k=8), 2, 5) != k1
+
+
+def test_candidates_by_regime(TU):
+    """Decode shapes: the shared caps and the per-expert tile classes applied
+    early; prefill shapes: caps of the shared and routed products crossed
+    with 256-row routed tiles on and off. The library's own choice is always
+    a candidate, and every candidate is a valid moe_tuning."""
+    from moe_expert_layer_fp32_amd import lib as L
+    from moe_inputs import get
+    dec = L.desc_from_config(get("dsv3_decode_share_bf16"))
+    pre = L.desc_from_config(get("prefill_zipf_bf16"))
+    for d, streams in ((dec, 2), (dec, 1), (pre, 2), (pre, 1)):
+        cands = TU.candidates_for(d, streams)
+        assert TU.limits() in cands
+        assert len({TU.label(c) for c in cands}) == len(cands)
+        for c in cands:
+            assert set(c) == set(TU.FIELDS) and all(v >= 0 for v in c.values())
+            TU.to_struct(c)
+    assert any(c["prefill_tokens"] == dec.T for c in TU.candidates_for(dec, 2))
+    pre2 = TU.candidates_for(pre, 2)
+    assert any(c["big_min_rows"] == TU.NO_BIG for c in pre2)
+    assert any(c["routed_ffn1_wgs"] > 0 for c in pre2) and any(c["shared_ffn1_wgs"] > 0 for c in pre2)
+    assert not any(c["shared_ffn1_wgs"] or c["routed_ffn1_wgs"] for c in TU.candidates_for(pre, 1))
+
+
+def test_merge_into_and_shipped_table(TU, tmp_path):
+    """Entries merged into a JSON table keep the others; the shipped table
+    loads and every entry in it is a complete, valid set of limits."""
+    p = tmp_path / "table.json"
+    TU.TilingCache({"a": {"limits": TU.limits(1), "us": {}}}).merge_into(str(p))
+    TU.TilingCache({"b": {"limits": TU.limits(2), "us": {}}}).merge_into(str(p))
+    t = TU.TilingCache.load(str(p))
+    assert t.lookup("a") == TU.limits(1) and t.lookup("b") == TU.limits(2)
+    shipped = TU.TilingCache.shipped()
+    for key, entry in shipped.table.items():
+        assert set(entry["limits"]) == set(TU.FIELDS), key
+        assert all(int(v) >= 0 for v in entry["limits"].values()), key
