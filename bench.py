@@ -40,7 +40,9 @@ INT8_PEAK_TOPS = 5000.0        # dense int8 matrix cores
 FP32_PEAK_TFLOPS = 157.3
 DEFAULT_CONFIG = "prefill_zipf_bf16"
 METRIC = "MoE-layer tokens/s at 1 GPU; decode HBM GB/s %peak; prefill MFMA %peak"
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "ffn1_traffic.json")
+def traffic_file(workload: str) -> str:
+    """Where the HBM traffic record of a workload's dominant launch lives."""
+    return os.path.join(ROOT, "profiles", f"{workload}_traffic.json")
 CSRC = os.path.join(ROOT, "moe_expert_layer_fp32_amd", "csrc")
 COPY_BYTES = 1 << 30
 
@@ -76,12 +78,14 @@ def parse():
                    help="with --traffic: which dispatch of that kernel within each layer call (0 = first)")
     p.add_argument("--traffic-per-call", type=int, default=1,
                    help="with --traffic: dispatches of that kernel per layer call")
+    p.add_argument("--traffic-launch", default="",
+                   help="with --traffic: which launch the record describes (shared_ffn1 or routed_ffn1)")
     return p.parse_args()
 
 
-# Sources that define the gate/up launch the traffic counters describe: its
-# kernel, the headers it includes, and the host code that sizes its launch.
-TRAFFIC_SOURCES = ("gemm_lds.hip", "tiles.h", "common.h", "kernels.h", "api.cpp")
+# Sources that define the launches the traffic counters describe: their
+# kernels, the headers they include, and the host code that sizes them.
+TRAFFIC_SOURCES = ("gemm_lds.hip", "gemm_big.hip", "tiles.h", "common.h", "kernels.h", "api.cpp")
 
 
 def kernel_hash() -> str:
@@ -103,7 +107,7 @@ def counter_values(path: str) -> dict:
     return out
 
 
-def traffic_record(paths, cfg_name: str, kernel: str, occurrence: int, per_call: int) -> dict:
+def traffic_record(paths, cfg_name: str, kernel: str, occurrence: int, per_call: int, launch: str) -> dict:
     """HBM bytes per launch of the dominant kernel from FETCH_SIZE and
     WRITE_SIZE (KiB per dispatch), each scaled by what the counter reads for a
     device copy of COPY_BYTES bytes (read COPY_BYTES, write COPY_BYTES). The
@@ -124,7 +128,7 @@ def traffic_record(paths, cfg_name: str, kernel: str, occurrence: int, per_call:
     w_sel = w_all[occurrence::per_call]
     fb = statistics.median(f_sel) * 1024.0 * f_scale
     wb = statistics.median(w_sel) * 1024.0 * w_scale
-    return {"workload": cfg_name, "kernel": name, "occurrence": occurrence, "per_call": per_call,
+    return {"workload": cfg_name, "launch": launch, "kernel": name, "occurrence": occurrence, "per_call": per_call,
             "dispatches": len(f_sel), "kernel_sha": kernel_hash(),
             "fetch_bytes_per_launch": fb, "write_bytes_per_launch": wb,
             "bytes_per_launch": fb + wb, "fetch_scale": f_scale, "write_scale": w_scale,
@@ -288,8 +292,8 @@ def main() -> int:
     args = parse()
     if args.traffic:
         rec = traffic_record(args.traffic, args.config, args.traffic_kernel, args.traffic_occurrence,
-                             args.traffic_per_call)
-        with open(TRAFFIC_FILE, "w") as f:
+                             args.traffic_per_call, args.traffic_launch)
+        with open(traffic_file(args.config), "w") as f:
             json.dump(rec, f, indent=1)
         print(json.dumps(rec))
         return 0
@@ -460,8 +464,8 @@ def main() -> int:
         roof = routed_roof
         roof_name = "routed_ffn1"
     roof["traffic"] = None
-    if os.path.exists(TRAFFIC_FILE):
-        tr = json.load(open(TRAFFIC_FILE))
+    if os.path.exists(traffic_file(cfg.name)):
+        tr = json.load(open(traffic_file(cfg.name)))
         if tr.get("kernel_sha") == kernel_hash() and tr.get("workload") == cfg.name and \
                 tr.get("launch") == roof_name:
             roof["traffic"] = tr.get("bytes_per_launch")
