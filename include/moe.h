@@ -179,9 +179,12 @@ typedef struct moe_tuning {
      *    experts are classed by their row count as below; with fewer, every
      *    expert takes 64-row tiles in one launch (the reduction split over
      *    workgroups when the experts alone are too few).
-     *  - stream_max_rows (theta): experts with at most this many rows stream
-     *    their weights through 64-row tiles (default 64); larger experts take
-     *    128-row tiles, or 256-row tiles from big_min_rows.
+     *  - stream_max_rows (theta): from prefill_tokens up, experts with at
+     *    most this many rows stream their weights through 64-row tiles
+     *    (default 64); larger experts take 128-row tiles, or 256-row tiles
+     *    from big_min_rows. Below prefill_tokens, a theta given here sends
+     *    experts with at most theta rows to the 32-row weight-streaming
+     *    kernel instead (none by default).
      *  - big_min_rows: bf16 experts with at least this many rows take the
      *    256-row tiles (default 256).
      *  - dense_big_rows: bf16 dense products (the shared expert) of at least

@@ -86,11 +86,14 @@ struct TilePolicy {
   int stream_max_rows = STREAM_MAX_ROWS;
   int big_min_rows = BIG_MIN_ROWS;
   int dense_big_rows = DENSE_BIG_ROWS;
+  // below the prefill threshold: experts with at most this many rows go to
+  // the 32-row weight-streaming kernel (0: none; only a caller's theta)
+  int decode_stream_rows = 0;
 };
 TilePolicy policy_of(const moe_tuning& t) {
   TilePolicy p;
   if (t.prefill_tokens > 0) p.prefill_tokens = t.prefill_tokens;
-  if (t.stream_max_rows > 0) p.stream_max_rows = t.stream_max_rows;
+  if (t.stream_max_rows > 0) p.stream_max_rows = p.decode_stream_rows = t.stream_max_rows;
   if (t.big_min_rows > 0) p.big_min_rows = t.big_min_rows;
   if (t.dense_big_rows > 0) p.dense_big_rows = t.dense_big_rows;
   return p;
@@ -371,6 +374,30 @@ moe_status run_routed(GemmArgs g, const moe_desc* d, GemmElem el, int planes, Ge
   // the reduction is split only at the default decode sizes (the workspace
   // holds the partial sums for exactly those)
   const int splits = prefill ? 1 : routed_splits(d, g.N, g.K);
+  if (!prefill && pol.decode_stream_rows > 0 && routed_tiled(d, g.N, g.K)) {
+    // Decode with a caller's theta: experts with at most theta rows stream
+    // their weights through the 32-row kernel (its matrix-core work covers
+    // only the row blocks an expert has), the others take the 64-row tiles
+    // (reduction split as without theta). Both launches pick their experts
+    // on the device from the offsets.
+    GemmArgs gs = g;
+    gs.max_group_rows = pol.decode_stream_rows;
+    gs.tiles_y = gemm_tiles_bound(r_max(d), g.n_groups);
+    gs.ksplit = gemm_stream_ksplit(long(g.n_groups) * (g.N / 16), g.K / kf_of(el));
+    HIP_TRY(launch_gemm(gs, el, planes, epi, s, KernelEvents{ev.start, nullptr}));
+    LdsArgs L{};
+    L.wave_features = 32;
+    L.splits = splits;
+    L.partial = partial;
+    L.part_rows = r_max(d);
+    L.max_wgs = capped_wgs(cap, splits);
+    L.tile_rows = 64;
+    L.min_rows = pol.decode_stream_rows + 1;
+    L.max_rows = INT32_MAX;
+    g.tiles_y = ceil_div(r_max(d), L.tile_rows) + g.n_groups;
+    HIP_TRY(launch_gemm_lds(g, L, el, planes, epi, s, KernelEvents{nullptr, ev.stop}));
+    return MOE_OK;
+  }
   if (splits > 1) {
     LdsArgs L{};
     L.wave_features = 32;

@@ -340,8 +340,11 @@ __device__ __forceinline__ void gemm_lds_tile(const GemmArgs& a, const LdsArgs& 
 // then share both the weights of a few column blocks and the activation
 // rows of a few m-tiles in its L2 (the order for dense products with many
 // m-tiles, whose activation rows are re-read once per column block).
+#ifndef MOE_RING_S2_BM64
+#define MOE_RING_S2_BM64 4
+#endif
 template <class Tr, int S, int EPI, int NF, int BM>
-constexpr int ring_steps() { return S == 1 || BM == 128 ? 8 : 4; }
+constexpr int ring_steps() { return S == 1 || BM == 128 ? 8 : MOE_RING_S2_BM64; }
 template <class Tr, int S, int EPI, int NF, int BM>
 constexpr int lds_waves_per_eu() { return BM == 64 && NF == 32 && ring_steps<Tr, S, EPI, NF, BM>() <= 8 ? 2 : 1; }
 

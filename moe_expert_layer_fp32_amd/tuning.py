@@ -57,6 +57,11 @@ def candidates_for(desc: L.MoeDesc, streams: int) -> list[dict]:
         for c in shared:
             out.append(limits(*c))
         out.append(limits(prefill_tokens=max(1, desc.T)))
+        best_caps = shared[-1] if len(shared) > 1 else (0, 0)
+        for theta in (32, 64):   # experts up to theta rows on the 32-row streaming kernel
+            out.append(limits(stream_max_rows=theta))
+            if best_caps != (0, 0):
+                out.append(limits(best_caps[0], best_caps[1], stream_max_rows=theta))
         return out
     shared = ((0, 0), (128, 128), (192, 192)) if (has_shared and streams == 2) else ((0, 0),)
     routed = ((0, 0), (160, 0)) if streams == 2 else ((0, 0),)

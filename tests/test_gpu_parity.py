@@ -935,6 +935,26 @@ def test_layer_launch_limits(name, caps):
     U.record(test="layer_launch_limits", cfg=name, caps=list(caps), err_vs_uncapped=dev)
 
 
+@pytest.mark.parametrize("name,theta", [("dsv3_decode_share_bf16", 32), ("pangu_moge_w8a8", 56),
+                                        ("longcat_zero_bf16", 20), ("tiny_fp32", 16)])
+def test_layer_decode_stream_theta(name, theta):
+    """Decode workloads with a caller's theta: experts with at most theta rows
+    go to the 32-row weight-streaming kernel, the others to the 64-row tiles
+    (split reduction where the layer uses one), chosen per expert on the
+    device; against the oracle, one and two streams."""
+    L, DeviceLayer, to_device = _L()
+    from moe_expert_layer_fp32_amd.layer import SecondStream
+    cfg, inp = U.inputs(name)
+    lay = U.device_layer(name)
+    t = L.MoeTuning(stream_max_rows=theta)
+    U.say(f"[gpu] layer {name} decode theta {theta}")
+    y = _check_layer(cfg, inp, lay, tuning=t)
+    if cfg.shared_inter:
+        y2 = lay.layer(second=SecondStream(), tuning=t)
+        torch.cuda.synchronize()
+        assert torch.equal(_bits(y), _bits(y2))
+
+
 def test_layer_largest_k_group_limited():
     """k = 16 (the largest built), group-limited selection of 4 of 8 groups
     over 256 experts, 16 resident, two streams."""
