@@ -371,11 +371,12 @@ def main() -> int:
     if args.limits:
         from moe_expert_layer_fp32_amd import tuning as TU
         lim = TU.limits(**json.loads(args.limits))
-        t_struct = TU.to_struct(lim)
+        t_struct = TU.to_struct(lim)     # None: every field 0, the library's own choice
+        tp = ctypes.pointer(t_struct) if t_struct is not None else None
         for a in auxes + ([warm_aux] if warm_aux is not None else []):
-            a.tuning = ctypes.pointer(t_struct)
+            a.tuning = tp
         if warm_aux is None:
-            warm_aux = L.MoeAux(tuning=ctypes.pointer(t_struct))
+            warm_aux = L.MoeAux(tuning=tp)
         tuned = {"limits": lim, "source": "--limits"}
     elif not args.no_tune:
         # The tiling table: the shipped entry for this shape, stream count and
