@@ -13,7 +13,8 @@
 // wavefront owns NF features), so they go straight from global memory into
 // a register ring 8 matrix-core steps deep, in the packed fragment layout: a
 // 32x32 operand is four 256-byte pieces of two adjacent 16-column fragments.
-// Each weight fragment is reused for BM rows.
+// Each weight fragment is reused for BM rows. Weights that only this tile
+// reads (its group has one m-tile) carry the nontemporal hint.
 //
 // Split-K: when rows x features give too few workgroups to fill the device
 // (decode-sized shared expert), the reduction is cut into `splits` ranges;
@@ -42,6 +43,11 @@ struct M32BF16 {
   __device__ static inline op_t load(const uint8_t* p) {
     return __builtin_bit_cast(op_t, *reinterpret_cast<const u32x4*>(p));
   }
+  template <bool NT>
+  __device__ static inline op_t load_w(const uint8_t* p) {
+    if constexpr (NT) return __builtin_bit_cast(op_t, __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p)));
+    return load(p);
+  }
 };
 struct M32I8 {
   using op_t = i32x4;
@@ -55,6 +61,11 @@ struct M32I8 {
   __device__ static inline op_t load(const uint8_t* p) {
     return __builtin_bit_cast(op_t, *reinterpret_cast<const u32x4*>(p));
   }
+  template <bool NT>
+  __device__ static inline op_t load_w(const uint8_t* p) {
+    if constexpr (NT) return __builtin_bit_cast(op_t, __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p)));
+    return load(p);
+  }
 };
 struct M32F32 {
   using op_t = float;
@@ -66,12 +77,17 @@ struct M32F32 {
     return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
   }
   __device__ static inline op_t load(const uint8_t* p) { return *reinterpret_cast<const float*>(p); }
+  template <bool NT>
+  __device__ static inline op_t load_w(const uint8_t* p) {
+    if constexpr (NT) return __builtin_nontemporal_load(reinterpret_cast<const float*>(p));
+    return load(p);
+  }
 };
 
 constexpr int CH_BYTES = 256;              // bytes of one row per LDS chunk
 constexpr int LDS_ROW = CH_BYTES + 16;     // padded row stride (4-bank shift per row)
 
-template <class Tr, int S, int EPI, int NF, int BM, int RA>
+template <class Tr, int S, int EPI, int NF, int BM, int RA, bool W_NT>
 __device__ __forceinline__ void gemm_lds_tile(const GemmArgs& a, const LdsArgs& L, uint8_t (&lds)[2][BM * LDS_ROW],
                                               int g, int row0, int nrows, int out0, int nblock, int split) {
   constexpr int FT = NF / 32;                  // 32-feature tiles per wavefront
@@ -119,7 +135,8 @@ __device__ __forceinline__ void gemm_lds_tile(const GemmArgs& a, const LdsArgs& 
     for (int f = 0; f < FT; ++f)
 #pragma unroll
       for (int s = 0; s < S; ++s)
-        aring[slot][f][s] = Tr::load(abase + (size_t(kt) * S + s) * FBW + size_t(2 * f) * FB + h * 2 * 16 * Tr::BPL);
+        aring[slot][f][s] = Tr::template load_w<W_NT>(abase + (size_t(kt) * S + s) * FBW + size_t(2 * f) * FB +
+                                                    h * 2 * 16 * Tr::BPL);
   };
 
 
@@ -380,8 +397,18 @@ void gemm_lds_kernel(GemmArgs a, LdsArgs L) {
     row0 = __builtin_amdgcn_readfirstlane(row0);
     nrows = __builtin_amdgcn_readfirstlane(nrows);
     out0 = __builtin_amdgcn_readfirstlane(out0);
-    gemm_lds_tile<Tr, S, EPI, NF, BM, ring_steps<Tr, S, EPI, NF, BM>()>(a, L, lds, g, row0, nrows, out0, nblock,
-                                                                          blockIdx.z);
+    // Weights of a group whose rows fit one m-tile are read by this tile
+    // alone (other tiles of the launch are other groups, other column
+    // blocks or other reduction slices): they are loaded with the
+    // nontemporal hint, which keeps them from displacing the activation rows
+    // (re-read by every column block) in the L2. Groups with several m-tiles
+    // re-read their weights and load them normally.
+    const bool once = a.offsets ? offs[g + 1] - offs[g] <= BM : a.dense_rows <= BM;
+    constexpr int RA = ring_steps<Tr, S, EPI, NF, BM>();
+    if (once)
+      gemm_lds_tile<Tr, S, EPI, NF, BM, RA, true>(a, L, lds, g, row0, nrows, out0, nblock, blockIdx.z);
+    else
+      gemm_lds_tile<Tr, S, EPI, NF, BM, RA, false>(a, L, lds, g, row0, nrows, out0, nblock, blockIdx.z);
   }
 }
 
