@@ -39,6 +39,7 @@ BF16_PEAK_TFLOPS = 2500.0      # dense bf16 matrix cores
 INT8_PEAK_TOPS = 5000.0        # dense int8 matrix cores
 FP32_PEAK_TFLOPS = 157.3
 DEFAULT_CONFIG = "prefill_zipf_bf16"
+COMPUTE_UNITS = 256
 METRIC = "MoE-layer tokens/s at 1 GPU; decode HBM GB/s %peak; prefill MFMA %peak"
 def traffic_file(workload: str) -> str:
     """Where the HBM traffic record of a workload's dominant launch lives."""
@@ -461,6 +462,13 @@ def main() -> int:
                                (", on the second stream beside the routed experts)" if second is not None
                                 else ")"))
         roof_name = "shared_ffn1"
+        # A cap on the shared gate/up's grid confines the launch to that many
+        # compute units (its 256-row tiles take one per workgroup); the
+        # fraction on those units says how well the tiles run there.
+        cap = int((tuned or {}).get("limits", {}).get("shared_ffn1_wgs", 0) or 0)
+        if second is not None and 0 < cap < COMPUTE_UNITS:
+            roof["compute_units"] = cap
+            roof["frac_on_its_compute_units"] = round(roof["frac"] * COMPUTE_UNITS / cap, 4)
     else:
         roof = routed_roof
         roof_name = "routed_ffn1"
