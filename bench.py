@@ -172,7 +172,7 @@ def shared_ffn1_algorithmic(cfg):
 
 
 def layer_algorithmic(cfg, counts_per_layer):
-    """Algorithmic work of one whole layer call (the survey's count):
+    """Algorithmic work of one whole layer call (the layer's own count):
     bytes = W1, W3 and W2 (and int8 scales) of every resident FFN expert that
     received tokens, the shared expert's weights, the fp32 router (4 d E) and
     x read plus y written (T d each, in the layer's element type); flops =
