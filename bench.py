@@ -136,23 +136,29 @@ def traffic_record(paths, cfg_name: str, kernel: str, occurrence: int, per_call:
             "copy_bytes": COPY_BYTES}
 
 
-def ffn1_algorithmic(cfg, counts_per_layer):
+# Launch-level algorithmic bytes follow the layer's rule (layer_algorithmic):
+# weights that must be read and the launch's input read once; the gathered
+# (permuted) rows and the h rows the launch writes are intermediates of this
+# implementation and are not counted.
+def ffn1_algorithmic(cfg, counts_per_layer, tokens_per_layer=None):
     """Algorithmic work of one launch of the routed gate/up projection:
-    bytes = W1 and W3 of every resident expert that received tokens, the R
-    gathered activation rows (d elements each) and the R rows of h written
-    (I elements each); flops = 2 * R * d * 2I."""
+    bytes = W1 and W3 (and int8 column scales) of every resident expert that
+    received tokens, plus the activation row of every token routed to one of
+    them read once (d elements: x, or its int8 codes in the W8A8 layer;
+    tokens_per_layer gives that token count, else all T); flops = 2 * R * d
+    * 2I."""
     wb = {"f32": 4, "bf16": 2, "w8a8": 1}[cfg.dtype]
     xb = {"f32": 4, "bf16": 2, "w8a8": 1}[cfg.dtype]
-    hb = {"f32": 4, "bf16": 2, "w8a8": 4}[cfg.dtype]
     out = []
-    for counts in counts_per_layer:
+    for li, counts in enumerate(counts_per_layer):
+        n_tok = cfg.T if tokens_per_layer is None else int(tokens_per_layer[li])
         res = counts[cfg.ffn_begin:cfg.ffn_begin + cfg.n_ffn]
         active = int((res > 0).sum())
         R = int(res.sum())
         wbytes = active * 2 * cfg.d * cfg.inter * wb
         if cfg.dtype == "w8a8":
             wbytes += active * 2 * cfg.inter * 4        # fp32 column scales
-        byts = wbytes + R * cfg.d * xb + R * cfg.inter * hb
+        byts = wbytes + n_tok * cfg.d * xb
         flops = 2.0 * R * cfg.d * 2 * cfg.inter
         out.append((byts, flops, R, active))
     return out
@@ -160,12 +166,11 @@ def ffn1_algorithmic(cfg, counts_per_layer):
 
 def shared_ffn1_algorithmic(cfg):
     """Algorithmic work of one launch of the shared expert's gate/up
-    projection (dense over all T tokens): bytes = its W1 and W3, x read once
-    and h written; flops = 2 * T * d * 2 I_s."""
+    projection (dense over all T tokens): bytes = its W1 and W3 (and int8
+    column scales) and the activations read once; flops = 2 * T * d * 2 I_s."""
     wb = {"f32": 4, "bf16": 2, "w8a8": 1}[cfg.dtype]
     xb = {"f32": 4, "bf16": 2, "w8a8": 1}[cfg.dtype]
-    hb = {"f32": 4, "bf16": 2, "w8a8": 4}[cfg.dtype]
-    byts = 2 * cfg.d * cfg.shared_inter * wb + cfg.T * cfg.d * xb + cfg.T * cfg.shared_inter * hb
+    byts = 2 * cfg.d * cfg.shared_inter * wb + cfg.T * cfg.d * xb
     if cfg.dtype == "w8a8":
         byts += 2 * cfg.shared_inter * 4
     return byts, 2.0 * cfg.T * cfg.d * 2 * cfg.shared_inter
@@ -338,10 +343,13 @@ def main() -> int:
 
     # Routing tables of each layer (outside the timed region) for the
     # algorithmic byte count of the dominant kernel.
-    counts_per_layer = []
+    counts_per_layer, routed_tokens = [], []
     for lay in layers:
         _, t = lay.layer_with_tables()
         counts_per_layer.append(t["counts"].cpu().numpy())
+        ids = t["topk_idx"].cpu().numpy()
+        resident = (ids >= cfg.ffn_begin) & (ids < cfg.ffn_begin + cfg.n_ffn)
+        routed_tokens.append(int(resident.any(axis=1).sum()))   # tokens with a resident selection
     torch.cuda.synchronize()
 
     K, W = args.steps, args.warmup
@@ -447,7 +455,7 @@ def main() -> int:
 
     bound = "mfma" if prefill else "hbm"
     ffn1_ms = np.array([a.elapsed_ms(b) for a, b in ev])
-    alg = ffn1_algorithmic(cfg, counts_per_layer)
+    alg = ffn1_algorithmic(cfg, counts_per_layer, routed_tokens)
     alg_bytes = np.array([alg[i % n_layers][0] for i in range(K)])
     alg_flops = np.array([alg[i % n_layers][1] for i in range(K)])
     routed_what = ("routed-expert gate/up projection + SwiGLU (" +

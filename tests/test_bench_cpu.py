@@ -66,8 +66,14 @@ def test_gate_up_bytes_and_flops():
     c = _all_active(cfg, rows_each=5)
     (byts, flops, R, active), = B.ffn1_algorithmic(cfg, [c])
     assert (R, active) == (5 * 64, 64)
-    assert byts == 64 * 2 * 1024 * 512 * 2 + R * 1024 * 2 + R * 512 * 2
+    # W1 and W3 of the 64 experts with tokens, x read once (256 rows); no
+    # gathered rows, no h
+    assert byts == 64 * 2 * 1024 * 512 * 2 + 256 * 1024 * 2
     assert flops == 2.0 * R * 1024 * 2 * 512
+    cfg = get("prefill_zipf_bf16")
+    sb, sf = B.shared_ffn1_algorithmic(cfg)
+    assert sb == 2 * 7168 * 2048 * 2 + 8192 * 7168 * 2
+    assert sf == 2.0 * 8192 * 7168 * 2 * 2048
 
 
 def test_bench_refuses_more_than_one_gpu():
