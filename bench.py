@@ -57,6 +57,8 @@ def parse():
     p.add_argument("--layers", type=int, default=0, help="layers cycled (0: enough for > 1 GB of weights)")
     p.add_argument("--cpu-seconds", type=float, default=10.0, help="target CPU time of the oracle sample")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-ceiling", action="store_true",
+                   help="skip the HBM read-ceiling measurement (moe_stream_read over 2 GiB)")
     p.add_argument("--no-tune", action="store_true",
                    help="skip choosing the launch limits from measured runs (tuning.py)")
     p.add_argument("--limits", default="",
@@ -197,6 +199,31 @@ def layer_algorithmic(cfg, counts_per_layer):
         flops = 2.0 * R * 3 * cfg.d * cfg.inter + 2.0 * cfg.T * 3 * cfg.d * cfg.shared_inter
         out.append((byts, flops))
     return out
+
+
+def hbm_read_ceiling(L, nbytes: int = 2 << 30, reps: int = 10) -> dict:
+    """The practical HBM read ceiling on this device: moe_stream_read (one
+    contiguous slice per workgroup, 16-byte loads) over a buffer well above
+    the 256 MB last-level cache, mean of `reps` back-to-back reads between two
+    events, after three untimed ones."""
+    import torch
+    buf = torch.ones(nbytes, dtype=torch.uint8, device="cuda")
+    sink = torch.empty(L.STREAM_READ_WGS, dtype=torch.int32, device="cuda")
+    for _ in range(3):
+        L.moe_stream_read(buf, nbytes, sink)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        L.moe_stream_read(buf, nbytes, sink)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    del buf
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    return {"achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+            "bytes": nbytes, "us": round(ms * 1e3, 1),
+            "kernel": f"moe_stream_read, {L.STREAM_READ_WGS} workgroups, one contiguous slice each"}
 
 
 def cpu_info() -> dict:
@@ -501,6 +528,14 @@ def main() -> int:
     layer_roof["alg_per_call"] = (float(np.mean([a[1] for a in lay_alg])) if prefill
                                   else int(np.mean([a[0] for a in lay_alg])))
 
+    ceiling = None
+    if not args.no_ceiling:
+        ceiling = hbm_read_ceiling(L)
+        if roof["bound"] == "hbm":
+            roof["frac_of_read_ceiling"] = round(roof["achieved"] / ceiling["achieved"], 4)
+        if layer_roof["bound"] == "hbm":
+            layer_roof["frac_of_read_ceiling"] = round(layer_roof["achieved"] / ceiling["achieved"], 4)
+
     graph = None
     if args.graph:
         graph = graph_replay(L, layers, desc, y, ws, second, K, t_struct if tuned else None)
@@ -531,6 +566,7 @@ def main() -> int:
         "layer_roofline": layer_roof,
         **({"routed_ffn1_roofline": routed_roof} if dom_shared else {}),
         "cpu_baseline": cpu,
+        **({"hbm_read_ceiling": ceiling} if ceiling is not None else {}),
     }
     if tuned is not None:
         rec["tuning"] = tuned

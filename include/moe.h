@@ -419,6 +419,24 @@ moe_status moe_layer(const moe_desc* desc, const moe_weights* w, const void* x,
 moe_status moe_layer_static(const moe_desc* desc, const moe_weights* w, const void* x, void* y,
                             moe_aux* aux, void* stream);
 
+/*
+ * Measurement helper, not a step of the layer: the practical HBM read
+ * ceiling against which the weight-streaming products are judged (the
+ * pages' decode analysis rests on weight movement being the bound: page
+ * "华为技术披露集 VOL.12：昇腾×盘古", section SwiftGMM; page
+ * "基于Atlas 900 A3 SuperPoD的LongCat-Flash模型推理性能优化实践", section
+ * 优化措施三). Reads every byte of the device buffer `buf` (`bytes` a
+ * multiple of 16, `buf` 16-byte aligned) once on `stream`, split into
+ * MOE_STREAM_READ_WGS contiguous slices, one per workgroup, and writes one
+ * 32-bit word per slice to the device array `sink` (MOE_STREAM_READ_WGS
+ * words, caller-owned): the XOR of that slice's 32-bit words, so the XOR of
+ * all sink words is the XOR of the whole buffer. Nothing else is written;
+ * bytes == 0 launches nothing. MOE_ERR_INVALID_ARG (before any launch) for a
+ * null pointer, a size not a multiple of 16 or a misaligned pointer.
+ */
+#define MOE_STREAM_READ_WGS 2048
+moe_status moe_stream_read(const void* buf, size_t bytes, void* sink, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -27,8 +27,10 @@ OP_ROUTE_TOPK, OP_PERMUTE, OP_FFN_ROUTED, OP_FFN_SHARED, OP_COMBINE, OP_LAYER = 
 
 # Every symbol include/moe.h declares.
 EXPORTS = ("moe_workspace_bytes", "moe_status_str", "moe_packed_bytes", "moe_pack_weights",
-           "moe_route_topk", "moe_permute", "moe_grouped_ffn", "moe_combine", "moe_layer", "moe_layer_static")
+           "moe_route_topk", "moe_permute", "moe_grouped_ffn", "moe_combine", "moe_layer", "moe_layer_static",
+           "moe_stream_read")
 STATIC_WORKSPACE_BYTES = 64 << 20   # MOE_STATIC_WORKSPACE_BYTES
+STREAM_READ_WGS = 2048              # MOE_STREAM_READ_WGS
 
 
 class MoeError(RuntimeError):
@@ -97,8 +99,9 @@ def load_library() -> ctypes.CDLL:
         lib.moe_combine.argtypes = [D, P, P, P, P, P, P, P, P, P]
         lib.moe_layer.argtypes = [D, W, P, P, ctypes.POINTER(MoeAux), P, ctypes.c_size_t, P]
         lib.moe_layer_static.argtypes = [D, W, P, P, ctypes.POINTER(MoeAux), P]
+        lib.moe_stream_read.argtypes = [P, ctypes.c_size_t, P, P]
         for fn in ("moe_pack_weights", "moe_route_topk", "moe_permute", "moe_grouped_ffn", "moe_combine",
-                   "moe_layer", "moe_layer_static"):
+                   "moe_layer", "moe_layer_static", "moe_stream_read"):
             getattr(lib, fn).restype = ctypes.c_int32
         _lib_handle = lib
     return _lib_handle
@@ -193,6 +196,10 @@ def moe_layer(desc, weights: MoeWeights, x, y, aux: MoeAux | None, ws, stream=No
     _check("moe_layer", load_library().moe_layer(
         _byref(desc), ctypes.byref(weights), ptr(x), ptr(y), ctypes.byref(aux) if aux is not None else None,
         ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(), stream_handle(stream)))
+
+
+def moe_stream_read(buf, nbytes: int, sink, stream=None) -> None:
+    _check("moe_stream_read", load_library().moe_stream_read(ptr(buf), nbytes, ptr(sink), stream_handle(stream)))
 
 
 def moe_layer_static(desc, weights: MoeWeights, x, y, aux: MoeAux | None, stream=None) -> None:

@@ -224,3 +224,21 @@ def test_static_workspace_size_matches_header(L):
     text = open(os.path.join(ROOT, "include", "moe.h"), encoding="utf-8").read()
     m = re.search(r"#define MOE_STATIC_WORKSPACE_BYTES \((\d+)u << (\d+)\)", text)
     assert m and int(m.group(1)) << int(m.group(2)) == L.STATIC_WORKSPACE_BYTES
+
+
+def test_stream_read_validates_before_any_launch(L):
+    """moe_stream_read: null pointers, a size not a multiple of 16 and a
+    misaligned buffer are MOE_ERR_INVALID_ARG before any launch; zero bytes
+    launch nothing."""
+    lib = L.load_library()
+    assert lib.moe_stream_read(None, 1 << 20, FAKE, None) == -1
+    assert lib.moe_stream_read(FAKE, 1 << 20, None, None) == -1
+    assert lib.moe_stream_read(FAKE, (1 << 20) + 8, FAKE, None) == -1
+    assert lib.moe_stream_read(FAKE + 4, 1 << 20, FAKE, None) == -1
+    assert lib.moe_stream_read(None, 0, None, None) == 0
+
+
+def test_stream_read_slices_match_header(L):
+    text = open(os.path.join(ROOT, "include", "moe.h"), encoding="utf-8").read()
+    m = re.search(r"#define MOE_STREAM_READ_WGS (\d+)", text)
+    assert m and int(m.group(1)) == L.STREAM_READ_WGS
