@@ -33,6 +33,7 @@ constexpr int PERM_WAVES = 16;
 constexpr int PERM_THREADS = PERM_WAVES * WAVE;
 constexpr int PERM_MAX_E = 256;
 constexpr int PERM_SEG_IDS = PERMUTE_ONE_WG / PERM_THREADS;   // ids per lane of a segment
+constexpr int PERM_BATCH = 16;   // chunk histograms read together
 static_assert(PERMUTE_CHUNK <= PERMUTE_ONE_WG, "a chunk must fit one workgroup's registers");
 
 // Histogram of the chunk [chunk * blockIdx.x, ...) of each workgroup into
@@ -102,12 +103,20 @@ __global__ __launch_bounds__(PERM_THREADS) void permute_kernel(const int* __rest
       total += c;
     }
     if (chunk_hist) {
+      // PERM_BATCH chunk counts loaded at once, then added in chunk order
+      // (one memory round trip per batch instead of one per chunk)
       const int nchunks = ceil_div(n, chunk);
       total = 0;
-      for (int b = 0; b < nchunks; ++b) {
-        const int c = chunk_hist[size_t(b) * E + e];
-        if (b < int(blockIdx.x)) before += c;
-        total += c;
+      for (int b0 = 0; b0 < nchunks; b0 += PERM_BATCH) {
+        int c[PERM_BATCH];
+#pragma unroll
+        for (int q = 0; q < PERM_BATCH; ++q)
+          c[q] = b0 + q < nchunks ? chunk_hist[size_t(b0 + q) * E + e] : 0;
+#pragma unroll
+        for (int q = 0; q < PERM_BATCH; ++q) {
+          if (b0 + q < int(blockIdx.x)) before += c[q];
+          total += c[q];
+        }
       }
     }
     if (blockIdx.x == 0) counts[e] = total;
