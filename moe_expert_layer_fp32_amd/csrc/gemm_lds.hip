@@ -412,6 +412,7 @@ void gemm_lds_kernel(GemmArgs a, LdsArgs L) {
   }
 }
 
+constexpr int REDUCE_BATCH = 4;
 // Sum of the split partials in split order, then the epilogue of the
 // product. One thread per 4 output columns of one row; rows of the selected
 // groups only.
@@ -419,12 +420,16 @@ template <typename PT, int EPI>
 __global__ __launch_bounds__(256) void gemm_reduce_kernel(GemmArgs a, LdsArgs L) {
   constexpr int NACC = (EPI == EPI_SWIGLU) ? 2 : 1;
   const int cols4 = a.N / 4;
+  // The groups' offsets in LDS: the row-to-group search below reads them
+  // there instead of making a dependent global round trip per step.
+  __shared__ int offs[TILE_MAX_GROUPS + 1];
+  stage_offsets(a, offs);
   // Rows to reduce: the compacted rows of the groups (known on the device
   // only), or the dense rows; a grid-stride loop covers them.
   int base = 0, rows = min(a.dense_rows, L.part_rows);
   if (a.offsets) {
-    base = a.offsets[a.first];
-    rows = min(a.offsets[a.first + a.n_groups] - base, L.part_rows);
+    base = offs[0];
+    rows = min(offs[a.n_groups] - base, L.part_rows);
   }
   const size_t total = size_t(rows) * cols4;
   for (size_t idx = blockIdx.x * size_t(blockDim.x) + threadIdx.x; idx < total;
@@ -438,10 +443,10 @@ __global__ __launch_bounds__(256) void gemm_reduce_kernel(GemmArgs a, LdsArgs L)
       int lo = 0, hi = a.n_groups - 1;   // last group whose start <= srow
       while (lo < hi) {
         const int mid = (lo + hi + 1) / 2;
-        if (a.offsets[a.first + mid] <= srow) lo = mid; else hi = mid - 1;
+        if (offs[mid] <= srow) lo = mid; else hi = mid - 1;
       }
       g = lo;
-      const int n = a.offsets[a.first + g + 1] - a.offsets[a.first + g];
+      const int n = offs[g + 1] - offs[g];
       if (n < L.min_rows || n > L.max_rows) continue;
       brow = a.sorted_slot ? a.sorted_slot[srow] / a.k : orow;
     }
@@ -449,11 +454,23 @@ __global__ __launch_bounds__(256) void gemm_reduce_kernel(GemmArgs a, LdsArgs L)
 #pragma unroll
     for (int s = 0; s < NACC; ++s) {
       PT t[4] = {0, 0, 0, 0};
-      for (int sp = 0; sp < L.splits; ++sp) {
-        const PT* P = reinterpret_cast<const PT*>(L.partial) + (size_t(sp) * L.part_rows + orow) * size_t(NACC) * a.N +
-                      size_t(s) * a.N + c0;
+      // REDUCE_BATCH slices loaded together (clamped slice index: every
+      // address is valid), then added in slice order
+      for (int sp0 = 0; sp0 < L.splits; sp0 += REDUCE_BATCH) {
+        PT q4[REDUCE_BATCH][4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) t[j] += P[j];
+        for (int b = 0; b < REDUCE_BATCH; ++b) {
+          const int sp = min(sp0 + b, L.splits - 1);
+          const PT* P = reinterpret_cast<const PT*>(L.partial) +
+                        (size_t(sp) * L.part_rows + orow) * size_t(NACC) * a.N + size_t(s) * a.N + c0;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) q4[b][j] = P[j];
+        }
+#pragma unroll
+        for (int b = 0; b < REDUCE_BATCH; ++b)
+          if (sp0 + b < L.splits)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) t[j] += q4[b][j];
       }
 #pragma unroll
       for (int j = 0; j < 4; ++j) sum[s][j] = float(t[j]);
