@@ -173,21 +173,41 @@ __device__ __forceinline__ void gemm_lds_tile(const GemmArgs& a, const LdsArgs& 
   // (int8: the threads at byte column 0 also fetch their row's activation
   // scale, which reaches the epilogue's lanes through LDS)
   __shared__ float bs_lds[BM];
+  // The rows' slot ids are loaded together (one round trip, not one per
+  // load: a test of the table pointer around each load made the compiler
+  // wait after each), then the row addresses and (int8) row scales follow.
   const uint8_t* bsrc[LOADS];
   int bdst[LOADS];
   float bsv[LOADS];
+  int brow[LOADS];
+#pragma unroll
+  for (int i = 0; i < LOADS; ++i) {
+    const int lin = threadIdx.x + i * WG_THREADS;
+    brow[i] = out0 + min(lin / (CH_BYTES / 16), nrows - 1);
+  }
+  if (a.sorted_slot) {
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) brow[i] = a.sorted_slot[row0 + (brow[i] - out0)];
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) brow[i] /= a.k;
+  }
 #pragma unroll
   for (int i = 0; i < LOADS; ++i) {
     const int lin = threadIdx.x + i * WG_THREADS;
     const int r = lin / (CH_BYTES / 16);
     const int col = (lin % (CH_BYTES / 16)) * 16;
-    const int rr = min(r, nrows - 1);
-    const int brow = a.sorted_slot ? a.sorted_slot[row0 + rr] / a.k : out0 + rr;
-    bsrc[i] = a.B + size_t(brow) * a.ldb + size_t(c_begin) * CH_BYTES + col;
+    bsrc[i] = a.B + size_t(brow[i]) * a.ldb + size_t(c_begin) * CH_BYTES + col;
     bdst[i] = r * LDS_ROW + col;
     bsv[i] = 1.f;
-    if constexpr (Tr::SCALED)
-      if (final_out && a.b_scale && col == 0) bsv[i] = a.b_scale[brow];
+  }
+  if constexpr (Tr::SCALED) {
+    if (final_out && a.b_scale) {
+#pragma unroll
+      for (int i = 0; i < LOADS; ++i) {
+        const float v = a.b_scale[brow[i]];
+        if (((threadIdx.x + i * WG_THREADS) % (CH_BYTES / 16)) == 0) bsv[i] = v;
+      }
+    }
   }
   float ep_bs[MBK];   // activation scale of epilogue row m * 32 + r32
 #pragma unroll
