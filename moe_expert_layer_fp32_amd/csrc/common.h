@@ -198,5 +198,12 @@ __device__ inline uint32_t wave_max_u32(uint32_t v) {
   v = max(v, dpp_u32<DPP_ROW_MIRROR>(v));
   return max(max(lane_u32(v, 0), lane_u32(v, 16)), max(lane_u32(v, 32), lane_u32(v, 48)));
 }
+__device__ inline uint32_t wave_min_u32(uint32_t v) {
+  v = min(v, dpp_u32<DPP_QUAD_1032>(v));
+  v = min(v, dpp_u32<DPP_QUAD_2301>(v));
+  v = min(v, dpp_u32<DPP_ROW_HALF_MIRROR>(v));
+  v = min(v, dpp_u32<DPP_ROW_MIRROR>(v));
+  return min(min(lane_u32(v, 0), lane_u32(v, 16)), min(lane_u32(v, 32), lane_u32(v, 48)));
+}
 
 }  // namespace moe

@@ -1,16 +1,17 @@
-// Gating and top-k selection for gfx950: one token per row of 16 lanes,
-// four tokens per wavefront.
+// Gating and top-k selection for gfx950: one token per wavefront.
 //
 // The router product leaves the logits z = x W_r + b in a [T][E_pad] buffer
 // (or split-K partial sums that are added here in split order, then the
-// bias). Lane r of a row holds experts r, r+16, r+32, ... (PL of them).
-// Scores are the softmax over the E logits or the logistic sigmoid of each
-// (the pages give no gate formula; which one a workload uses is part of its
-// descriptor). Every reduction stays inside the row, as data-parallel moves
-// after which all 16 lanes hold the result, so rounds cost a few
-// instructions and never leave the vector unit. A selection round is an
-// argmax: the largest order-preserving bits of the logit, then the lowest
-// expert id holding them (equal logits go to the lower id):
+// bias). Lane l of the wavefront holds experts 4l .. 4l+3 (E <= 256), so a
+// token's logits arrive in one 16-byte load per lane and split. Scores are
+// the softmax over the E logits or the logistic sigmoid of each (the pages
+// give no gate formula; which one a workload uses is part of its
+// descriptor). Every reduction is over the whole wavefront: data-parallel
+// moves inside each row of 16 lanes, then the four row results read into
+// scalar registers, so each round's winner is one value shared by the
+// wavefront. A selection round is an argmax: the largest order-preserving
+// bits of the logit, then the lowest expert id holding them (equal logits
+// go to the lower id):
 //  - plain top-k: k rounds over all experts;
 //  - group-limited: group scores (sum of the two largest scores of each
 //    contiguous group), topk_group rounds over the groups, then k rounds over
@@ -21,6 +22,11 @@
 // Softmax and sigmoid are monotone, so selecting on the logit is selecting
 // on the score. Weights are the selected scores, renormalised over the k
 // selections when asked, times route_scale.
+//
+// One token per wavefront (not four tokens on rows of 16 lanes) keeps each
+// lane's share of a round to four experts and puts four times as many
+// wavefronts to work on the same tokens; the rounds are chains of dependent
+// steps, so the shorter chain is what counts.
 #include <type_traits>
 
 #include "common.h"
@@ -28,58 +34,60 @@
 
 namespace moe {
 
-constexpr int ROW = 16;            // lanes per token
-constexpr int GATE_TOKENS = WAVE / ROW;
-constexpr int GROUP_SLOTS = 4;     // group-limited routing: n_group <= 64
-constexpr int GATE_SPLIT_BATCH = 4;  // split-K partial sums loaded together
+constexpr int GATE_SLOTS = 4;                    // experts per lane: lane l holds 4l .. 4l+3
+constexpr int GATE_MAX_E = GATE_SLOTS * WAVE;    // 256
+constexpr int GATE_MAX_GROUPS = WAVE;            // group g's score sits in lane g
 
 __device__ inline uint32_t order_bits(float f) {
   const uint32_t b = __float_as_uint(f + 0.0f);   // -0 -> +0
   return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
 }
 
-// Reductions over the 16 lanes of a row; every lane of the row gets the result.
-__device__ inline uint32_t row_max_u32(uint32_t v) {
-  v = max(v, dpp_u32<DPP_QUAD_1032>(v));
-  v = max(v, dpp_u32<DPP_QUAD_2301>(v));
-  v = max(v, dpp_u32<DPP_ROW_HALF_MIRROR>(v));
-  return max(v, dpp_u32<DPP_ROW_MIRROR>(v));
-}
-__device__ inline uint32_t row_min_u32(uint32_t v) {
-  v = min(v, dpp_u32<DPP_QUAD_1032>(v));
-  v = min(v, dpp_u32<DPP_QUAD_2301>(v));
-  v = min(v, dpp_u32<DPP_ROW_HALF_MIRROR>(v));
-  return min(v, dpp_u32<DPP_ROW_MIRROR>(v));
-}
-__device__ inline float row_max_f32(float v) {
-  return row_reduce_f32(v, [](float x, float y) { return fmaxf(x, y); });
-}
-__device__ inline float row_sum_f32(float v) {
-  return row_reduce_f32(v, [](float x, float y) { return x + y; });
+// One selection round over keys (a candidate's order bits; 0 for no
+// candidate): the largest key, then the lowest id holding it (slot j of
+// lane l is id l*N + j, so that is the lowest lane holding it, then its
+// lowest slot). The winner's key is set to 0 and its id returned, the same
+// in every lane; -1 when no candidate is left (every finite logit has order
+// bits above 0). All lanes active.
+template <int N>
+__device__ inline int wave_take_max(uint32_t (&key)[N], int lane) {
+  uint32_t m = key[0];
+#pragma unroll
+  for (int j = 1; j < N; ++j) m = max(m, key[j]);
+  m = wave_max_u32(m);
+  if (m == 0) return -1;
+  int slot = N;
+#pragma unroll
+  for (int j = N - 1; j >= 0; --j)
+    if (key[j] == m) slot = j;
+  const uint64_t holders = __builtin_amdgcn_ballot_w64(slot < N);
+  const int wl = __builtin_ctzll(holders);
+  const int ws = __builtin_amdgcn_readlane(slot, wl);
+#pragma unroll
+  for (int j = 0; j < N; ++j)
+    if (lane == wl && j == ws) key[j] = 0;
+  return wl * N + ws;
 }
 
-// Lowest id (slot i of lane r is id i*16 + r) among the candidates holding
-// the largest order bits; -1 when there is no candidate (every finite logit
-// has order bits above 0).
-template <int N>
-__device__ inline int row_argmax(const uint32_t (&ob)[N], const bool (&cand)[N], int r) {
-  uint32_t m = 0;
-#pragma unroll
-  for (int i = 0; i < N; ++i) m = max(m, cand[i] ? ob[i] : 0u);
-  m = row_max_u32(m);
-  uint32_t best = 0xFFFFFFFFu;
-#pragma unroll
-  for (int i = N - 1; i >= 0; --i)
-    if (cand[i] && ob[i] == m) best = uint32_t(i * ROW + r);
-  best = row_min_u32(best);
-  return m == 0 ? -1 : int(best);
+// Inside aligned blocks of L lanes (L a power of two, at most 16): the
+// largest key and the lowest id holding it, in every lane of the block.
+__device__ inline void pick_better(uint32_t& k, int& id, uint32_t pk, int pid) {
+  if (pk > k || (pk == k && pid < id)) {
+    k = pk;
+    id = pid;
+  }
 }
-
-template <int N>
-__device__ inline void drop(bool (&cand)[N], int id, int r) {
-#pragma unroll
-  for (int i = 0; i < N; ++i)
-    if (i * ROW + r == id) cand[i] = false;
+template <int CTRL>
+__device__ inline void pick_better_dpp(uint32_t& k, int& id) {
+  const uint32_t pk = dpp_u32<CTRL>(k);
+  const int pid = int(dpp_u32<CTRL>(uint32_t(id)));
+  pick_better(k, id, pk, pid);
+}
+__device__ inline void block_argmax(uint32_t& k, int& id, int L) {
+  if (L >= 2) pick_better_dpp<DPP_QUAD_1032>(k, id);
+  if (L >= 4) pick_better_dpp<DPP_QUAD_2301>(k, id);
+  if (L >= 8) pick_better_dpp<DPP_ROW_HALF_MIRROR>(k, id);
+  if (L >= 16) pick_better_dpp<DPP_ROW_MIRROR>(k, id);
 }
 
 // Top two of (a1 >= a2) and (b1 >= b2).
@@ -96,248 +104,229 @@ __device__ inline void merge_top2_dpp(float& t1, float& t2) {
   const float b1 = dpp_f32<CTRL>(t1), b2 = dpp_f32<CTRL>(t2);
   merge_top2(t1, t2, b1, b2);
 }
-
-// FW wavefronts per workgroup. With split-K partial sums FW > 1: wavefront w
-// adds splits w, w + FW, ... (in that order) for the workgroup's four tokens,
-// the FW sums meet in LDS and are added in wavefront order; then only the
-// first wavefront runs the gate (the others leave after the fold's barrier,
-// so they do not share its SIMD with copies of the same work).
-// Gate and selection for one token held by a row of 16 lanes (lane r holds
-// experts i*16 + r). u: its logits, bias included. sc_row: the row's LDS
-// scratch for its scores (written and read by this wavefront only). Lane
-// r < k gets selection r: sel_out (expert id) and w_out (its weight). Every
-// lane of the wavefront must be active.
-template <int PL>
-__device__ __forceinline__ void gate_row(const GateArgs& a, float (&u)[PL], const bool (&valid)[PL], int r,
-                                         float* sc_row, int& sel_out, float& w_out) {
-  float sc[PL];
-  uint32_t ob[PL];
-  int grp[PL];
+// The two largest of every lane's (t1 >= t2), the same pair in every lane.
+__device__ inline void wave_top2(float& t1, float& t2) {
+  merge_top2_dpp<DPP_QUAD_1032>(t1, t2);
+  merge_top2_dpp<DPP_QUAD_2301>(t1, t2);
+  merge_top2_dpp<DPP_ROW_HALF_MIRROR>(t1, t2);
+  merge_top2_dpp<DPP_ROW_MIRROR>(t1, t2);
+  float a1 = lane_f32(t1, 0), a2 = lane_f32(t2, 0);
 #pragma unroll
-  for (int i = 0; i < PL; ++i) {
-    if (!valid[i]) u[i] = -INFINITY;
-    ob[i] = order_bits(u[i]);
+  for (int row = 1; row < WAVE / 16; ++row) merge_top2(a1, a2, lane_f32(t1, 16 * row), lane_f32(t2, 16 * row));
+  t1 = a1;
+  t2 = a2;
+}
+
+// N split-K partial sums (16 bytes per lane each) loaded together, then
+// added to acc in split order.
+template <int N>
+__device__ inline void fold_splits(const float* p, size_t split_stride, int sp0, f32x4& acc) {
+  f32x4 part[N];
+#pragma unroll
+  for (int q = 0; q < N; ++q) part[q] = *reinterpret_cast<const f32x4*>(p + size_t(sp0 + q) * split_stride);
+  __builtin_amdgcn_sched_barrier(0);   // every load issued before the first add
+#pragma unroll
+  for (int q = 0; q < N; ++q) acc += part[q];
+}
+
+// GW wavefronts per workgroup, one token each; every wavefront works alone
+// (its own LDS row, no barrier).
+template <int GW>
+__global__ __launch_bounds__(GW * WAVE) void gate_topk_kernel(GateArgs a) {
+  __shared__ __align__(16) float sc_lds[GW][GATE_MAX_E];
+  const int lane = threadIdx.x & (WAVE - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / WAVE);
+  const int t = blockIdx.x * GW + wave;
+  if (t >= a.T) return;   // whole wavefront
+  const int e0 = GATE_SLOTS * lane;
+  const int col = min(e0, a.ldz - GATE_SLOTS);   // lanes past the row read its last 16 bytes
+  float* sc_row = &sc_lds[wave][0];
+
+  f32x4 z4;
+  if (!a.partial) {
+    z4 = *reinterpret_cast<const f32x4*>(a.z + size_t(t) * a.ldz + col);
+  } else {
+    // split order: splits 0, 1, 2, ... added one after another
+    z4 = f32x4{0.f, 0.f, 0.f, 0.f};
+    const float* P = a.partial + size_t(t) * a.ldz + col;
+    const size_t ss = size_t(a.T) * a.ldz;
+    int sp = 0;
+    for (; sp + 16 <= a.splits; sp += 16) fold_splits<16>(P, ss, sp, z4);
+    if (sp + 8 <= a.splits) { fold_splits<8>(P, ss, sp, z4); sp += 8; }
+    if (sp + 4 <= a.splits) { fold_splits<4>(P, ss, sp, z4); sp += 4; }
+    if (sp + 2 <= a.splits) { fold_splits<2>(P, ss, sp, z4); sp += 2; }
+    if (sp < a.splits) fold_splits<1>(P, ss, sp, z4);
+    if (a.bias) {
+      // all four loads issued before any is used (clamped index, no per-slot branch)
+      float bv[GATE_SLOTS];
+#pragma unroll
+      for (int j = 0; j < GATE_SLOTS; ++j) bv[j] = a.bias[min(e0 + j, a.E - 1)];
+#pragma unroll
+      for (int j = 0; j < GATE_SLOTS; ++j) z4[j] += bv[j];
+    }
+  }
+
+  float u[GATE_SLOTS], sc[GATE_SLOTS];
+  bool valid[GATE_SLOTS];
+  uint32_t ob[GATE_SLOTS];
+#pragma unroll
+  for (int j = 0; j < GATE_SLOTS; ++j) {
+    valid[j] = e0 + j < a.E;
+    u[j] = valid[j] ? z4[j] : -INFINITY;
+    ob[j] = order_bits(u[j]);
   }
 
   if (a.gate == MOE_GATE_SOFTMAX) {
     float m = -INFINITY;
 #pragma unroll
-    for (int i = 0; i < PL; ++i) m = fmaxf(m, u[i]);
-    m = row_max_f32(m);
+    for (int j = 0; j < GATE_SLOTS; ++j) m = fmaxf(m, u[j]);
+    m = wave_max(m);
     float sum = 0.f;
 #pragma unroll
-    for (int i = 0; i < PL; ++i) {
-      sc[i] = valid[i] ? expf(u[i] - m) : 0.f;
-      sum += sc[i];
+    for (int j = 0; j < GATE_SLOTS; ++j) {
+      sc[j] = valid[j] ? expf(u[j] - m) : 0.f;
+      sum += sc[j];
     }
-    sum = row_sum_f32(sum);
+    sum = wave_sum(sum);
 #pragma unroll
-    for (int i = 0; i < PL; ++i) sc[i] = sc[i] / sum;
+    for (int j = 0; j < GATE_SLOTS; ++j) sc[j] = sc[j] / sum;
   } else {
 #pragma unroll
-    for (int i = 0; i < PL; ++i) sc[i] = valid[i] ? 1.0f / (1.0f + expf(-u[i])) : 0.f;
+    for (int j = 0; j < GATE_SLOTS; ++j) sc[j] = valid[j] ? 1.0f / (1.0f + expf(-u[j])) : 0.f;
   }
-#pragma unroll
-  for (int i = 0; i < PL; ++i) sc_row[i * ROW + r] = sc[i];
+  *reinterpret_cast<f32x4*>(sc_row + e0) = f32x4{sc[0], sc[1], sc[2], sc[3]};
 
-  bool cand[PL];
+  // key[j]: the slot's order bits while it is a candidate, else 0
+  uint32_t key[GATE_SLOTS];
 #pragma unroll
-  for (int i = 0; i < PL; ++i) cand[i] = valid[i];
+  for (int j = 0; j < GATE_SLOTS; ++j) key[j] = valid[j] ? ob[j] : 0u;
 
   if (a.topk_group > 0 || a.per_group_k > 0) {
     const int gsize = a.E / a.n_group;
+    // Aligned groups: every group is L whole lanes (L a power of two, at
+    // most 16), so a lane's four slots share one group and a group's
+    // reductions stay inside its own lanes.
+    const int L = gsize / GATE_SLOTS;
+    const bool aligned = gsize % GATE_SLOTS == 0 && L <= 16 && (L & (L - 1)) == 0;
+    int grp[GATE_SLOTS];   // the slot's group; 0 for slots past E (never candidates)
 #pragma unroll
-    for (int i = 0; i < PL; ++i) grp[i] = valid[i] ? (i * ROW + r) / gsize : -1;
-  }
-  if (a.topk_group > 0) {
-    // group g's score = sum of its two largest scores; slot g/16 of lane g%16
-    float gs[GROUP_SLOTS];
-    bool gc[GROUP_SLOTS];
+    for (int j = 0; j < GATE_SLOTS; ++j) grp[j] = valid[j] ? (e0 + j) / gsize : 0;
+
+    if (a.topk_group > 0) {
+      // group g's score: the sum of its two largest scores
+      uint32_t gkey[1];
+      int gdiv;   // a winning lane's group is lane / gdiv
+      if (aligned) {
+        float t1 = -INFINITY, t2 = -INFINITY;
 #pragma unroll
-    for (int j = 0; j < GROUP_SLOTS; ++j) {
-      gs[j] = -INFINITY;
-      gc[j] = j * ROW + r < a.n_group;
-    }
-    auto finish_group = [&](int g, float t1, float t2) {
-      merge_top2_dpp<DPP_QUAD_1032>(t1, t2);
-      merge_top2_dpp<DPP_QUAD_2301>(t1, t2);
-      merge_top2_dpp<DPP_ROW_HALF_MIRROR>(t1, t2);
-      merge_top2_dpp<DPP_ROW_MIRROR>(t1, t2);
+        for (int j = 0; j < GATE_SLOTS; ++j)
+          if (valid[j]) merge_top2(t1, t2, sc[j], -INFINITY);
+        if (L >= 2) merge_top2_dpp<DPP_QUAD_1032>(t1, t2);
+        if (L >= 4) merge_top2_dpp<DPP_QUAD_2301>(t1, t2);
+        if (L >= 8) merge_top2_dpp<DPP_ROW_HALF_MIRROR>(t1, t2);
+        if (L >= 16) merge_top2_dpp<DPP_ROW_MIRROR>(t1, t2);
+        // the first lane of each group stands for it
+        gkey[0] = (lane % L == 0 && lane / L < a.n_group) ? order_bits(t1 + t2) : 0u;
+        gdiv = L;
+      } else {
+        float gv = -INFINITY;   // lane g: group g's score
+        for (int g = 0; g < a.n_group; ++g) {
+          float t1 = -INFINITY, t2 = -INFINITY;
 #pragma unroll
-      for (int j = 0; j < GROUP_SLOTS; ++j)
-        if (j * ROW + r == g) gs[j] = t1 + t2;
-    };
-    const int gsize = a.E / a.n_group;
-    const int spg = gsize / ROW;   // slots per group when groups are whole slots
-    if (gsize >= ROW && gsize % ROW == 0 && a.E % ROW == 0) {
-      // Slot i of every lane holds experts i*16 .. i*16+15, all in group
-      // i / spg: one pass over the slots, a group closed after its last slot
-      // (a wave-uniform branch).
-      float t1 = -INFINITY, t2 = -INFINITY;
+          for (int j = 0; j < GATE_SLOTS; ++j)
+            if (valid[j] && grp[j] == g) merge_top2(t1, t2, sc[j], -INFINITY);
+          wave_top2(t1, t2);
+          if (lane == g) gv = t1 + t2;
+        }
+        gkey[0] = lane < a.n_group ? order_bits(gv) : 0u;
+        gdiv = 1;
+      }
+      uint64_t kept = 0;
+      for (int q = 0; q < a.topk_group; ++q) {
+        const int gw = wave_take_max<1>(gkey, lane);
+        if (gw < 0) break;
+        kept |= 1ull << (gw / gdiv);
+      }
 #pragma unroll
-      for (int i = 0; i < PL; ++i) {
-        if (i * ROW < a.E) {
-          merge_top2(t1, t2, sc[i], -INFINITY);
-          if ((i + 1) % spg == 0) {
-            finish_group(i / spg, t1, t2);
-            t1 = t2 = -INFINITY;
+      for (int j = 0; j < GATE_SLOTS; ++j)
+        if (!((kept >> grp[j]) & 1ull)) key[j] = 0u;
+    } else {
+      // per_group_k largest of each group (ties to the lower id)
+      bool chosen[GATE_SLOTS];
+#pragma unroll
+      for (int j = 0; j < GATE_SLOTS; ++j) chosen[j] = false;
+      if (aligned) {
+        // the groups' rounds run side by side, one round per quota step
+        for (int q = 0; q < a.per_group_k; ++q) {
+          uint32_t bk = 0u;
+          int bid = e0;
+#pragma unroll
+          for (int j = GATE_SLOTS - 1; j >= 0; --j)
+            if (!chosen[j] && key[j] >= bk) {
+              bk = key[j];
+              bid = e0 + j;
+            }
+          block_argmax(bk, bid, L);
+#pragma unroll
+          for (int j = 0; j < GATE_SLOTS; ++j)
+            if (bk != 0u && e0 + j == bid) chosen[j] = true;
+        }
+      } else {
+        for (int g = 0; g < a.n_group; ++g) {
+          uint32_t in_g[GATE_SLOTS];
+#pragma unroll
+          for (int j = 0; j < GATE_SLOTS; ++j) in_g[j] = grp[j] == g ? key[j] : 0u;
+          for (int q = 0; q < a.per_group_k; ++q) {
+            const int win = wave_take_max<GATE_SLOTS>(in_g, lane);
+            if (win < 0) break;
+#pragma unroll
+            for (int j = 0; j < GATE_SLOTS; ++j)
+              if (e0 + j == win) chosen[j] = true;
           }
         }
       }
-    } else {
-      for (int g = 0; g < a.n_group; ++g) {
-        float t1 = -INFINITY, t2 = -INFINITY;
 #pragma unroll
-        for (int i = 0; i < PL; ++i)
-          if (grp[i] == g) merge_top2(t1, t2, sc[i], -INFINITY);
-        finish_group(g, t1, t2);
-      }
+      for (int j = 0; j < GATE_SLOTS; ++j)
+        if (!chosen[j]) key[j] = 0u;
     }
-    uint32_t gob[GROUP_SLOTS];
-#pragma unroll
-    for (int j = 0; j < GROUP_SLOTS; ++j) gob[j] = order_bits(gs[j]);
-    uint64_t kept = 0;
-    for (int q = 0; q < a.topk_group; ++q) {
-      const int gw = row_argmax(gob, gc, r);
-      if (gw < 0) break;
-      kept |= 1ull << gw;
-      drop(gc, gw, r);
-    }
-#pragma unroll
-    for (int i = 0; i < PL; ++i) cand[i] = valid[i] && ((kept >> grp[i]) & 1ull);
-  } else if (a.per_group_k > 0) {
-    bool chosen[PL];
-#pragma unroll
-    for (int i = 0; i < PL; ++i) chosen[i] = false;
-    for (int g = 0; g < a.n_group; ++g) {
-      bool in_g[PL];
-#pragma unroll
-      for (int i = 0; i < PL; ++i) in_g[i] = grp[i] == g;
-      for (int q = 0; q < a.per_group_k; ++q) {
-        const int win = row_argmax(ob, in_g, r);
-        if (win < 0) break;
-        drop(in_g, win, r);
-#pragma unroll
-        for (int i = 0; i < PL; ++i)
-          if (i * ROW + r == win) chosen[i] = true;
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < PL; ++i) cand[i] = chosen[i];
   }
 
   // k rounds over the candidates: descending logit, ties to the lower id;
-  // lane r of the row keeps selection r.
+  // lane j keeps selection j.
   int sel_e = -1;
   for (int j = 0; j < a.k; ++j) {
-    const int win = row_argmax(ob, cand, r);
+    const int win = wave_take_max<GATE_SLOTS>(key, lane);
     if (win < 0) break;
-    drop(cand, win, r);
-    if (r == j) sel_e = win;
+    if (lane == j) sel_e = win;
   }
-  __threadfence_block();   // the row's scores are in LDS (written by this wavefront)
-  const bool mine = r < a.k && sel_e >= 0;
+  __threadfence_block();   // the scores are in LDS (written by this wavefront)
+  const bool mine = lane < a.k && sel_e >= 0;
   const float s = mine ? sc_row[sel_e] : 0.f;
-  const float total = row_sum_f32(s);
-  sel_out = sel_e;
-  w_out = (a.renorm ? s / total : s) * a.route_scale;
-}
-
-
-template <int PL, int FW>
-__global__ __launch_bounds__(FW * WAVE) void gate_topk_kernel(GateArgs a) {
-  __shared__ float sc_lds[GATE_TOKENS][PL * ROW];
-  __shared__ float fold[FW][GATE_TOKENS][PL * ROW];
-  const int lane = threadIdx.x & (WAVE - 1);
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / WAVE);
-  const int r = lane & (ROW - 1), row = lane / ROW;
-  const int t_raw = blockIdx.x * GATE_TOKENS + row;
-  const bool live = t_raw < a.T;            // dead rows work on a valid token and write nothing
-  const int t = live ? t_raw : a.T - 1;
-
-  float u[PL];
-  bool valid[PL];
-#pragma unroll
-  for (int i = 0; i < PL; ++i) {
-    const int e = i * ROW + r;
-    valid[i] = e < a.E;
-    u[i] = 0.f;
-  }
-  if (!a.partial) {
-#pragma unroll
-    for (int i = 0; i < PL; ++i)
-      if (valid[i]) u[i] = a.z[size_t(t) * a.ldz + i * ROW + r];
-  } else {
-    // This wavefront's splits, GATE_SPLIT_BATCH loads at a time (clamped
-    // split index: every address is valid; absent splits add +0).
-    float mine[PL];
-#pragma unroll
-    for (int i = 0; i < PL; ++i) mine[i] = 0.f;
-    for (int sp0 = wave; sp0 < a.splits; sp0 += GATE_SPLIT_BATCH * FW) {
-      float part[GATE_SPLIT_BATCH][PL];
-#pragma unroll
-      for (int q = 0; q < GATE_SPLIT_BATCH; ++q) {
-        const float* P = a.partial + (size_t(min(sp0 + q * FW, a.splits - 1)) * a.T + t) * a.ldz + r;
-#pragma unroll
-        for (int i = 0; i < PL; ++i) part[q][i] = P[min(i * ROW, a.ldz - ROW)];
-      }
-#pragma unroll
-      for (int q = 0; q < GATE_SPLIT_BATCH; ++q)
-#pragma unroll
-        for (int i = 0; i < PL; ++i) mine[i] += (sp0 + q * FW < a.splits && valid[i]) ? part[q][i] : 0.f;
-    }
-    if (FW == 1) {
-#pragma unroll
-      for (int i = 0; i < PL; ++i) u[i] = mine[i];
-    } else {
-#pragma unroll
-      for (int i = 0; i < PL; ++i) fold[wave][row][i * ROW + r] = mine[i];
-      __syncthreads();
-#pragma unroll
-      for (int w = 0; w < FW; ++w)
-#pragma unroll
-        for (int i = 0; i < PL; ++i) u[i] += fold[w][row][i * ROW + r];
-    }
-    if (a.bias) {
-#pragma unroll
-      for (int i = 0; i < PL; ++i)
-        if (valid[i]) u[i] += a.bias[i * ROW + r];
-    }
-  }
-  if (FW > 1 && wave != 0) return;   // no barrier follows
-  int sel_e;
-  float wv;
-  gate_row<PL>(a, u, valid, r, &sc_lds[row][0], sel_e, wv);
-  if (live && r < a.k) {
-    a.topk_idx[size_t(t) * a.k + r] = sel_e;
-    a.topk_w[size_t(t) * a.k + r] = wv;
+  const float total = wave_sum(s);
+  const float wv = (a.renorm ? s / total : s) * a.route_scale;
+  if (lane < a.k) {
+    a.topk_idx[size_t(t) * a.k + lane] = sel_e;
+    a.topk_w[size_t(t) * a.k + lane] = wv;
   }
 }
 
-constexpr int GATE_FOLD_WAVES = 8;
-template <int PL>
-static hipError_t launch_gate_pl(const GateArgs& a, hipStream_t stream) {
-  const dim3 grid(ceil_div(a.T, GATE_TOKENS));
-  // Folding over several wavefronts pays for few tokens with many splits;
-  // for many tokens the redundant gate work of the extra wavefronts costs more.
-  if (a.partial && a.splits > 2 && a.T <= 2048)
-    hipLaunchKernelGGL((gate_topk_kernel<PL, GATE_FOLD_WAVES>), grid, dim3(GATE_FOLD_WAVES * WAVE), 0, stream, a);
-  else
-    hipLaunchKernelGGL((gate_topk_kernel<PL, 1>), grid, dim3(WAVE), 0, stream, a);
-  return hipGetLastError();
-}
+// Four tokens per workgroup from GATE_WIDE_FROM tokens (fewer, larger
+// workgroups); below, one token per workgroup spreads the few tokens over
+// more compute units.
+constexpr int GATE_WIDE_FROM = 2048;
+constexpr int GATE_WIDE = 4;
 
 hipError_t launch_gate(const GateArgs& a, hipStream_t stream) {
   if (a.T <= 0) return hipSuccess;
   if (a.partial && a.splits < 1) return hipErrorInvalidValue;
-  const int pl = ceil_div(a.E, ROW);
-  if (pl <= 1) return launch_gate_pl<1>(a, stream);
-  if (pl <= 2) return launch_gate_pl<2>(a, stream);
-  if (pl <= 4) return launch_gate_pl<4>(a, stream);
-  if (pl <= 6) return launch_gate_pl<6>(a, stream);
-  if (pl <= 8) return launch_gate_pl<8>(a, stream);
-  if (pl <= 12) return launch_gate_pl<12>(a, stream);
-  return launch_gate_pl<16>(a, stream);
+  if (a.E < 1 || a.E > GATE_MAX_E || a.ldz < a.E || a.ldz % GATE_SLOTS != 0) return hipErrorInvalidValue;
+  if ((a.topk_group > 0 || a.per_group_k > 0) && (a.n_group < 1 || a.E % a.n_group != 0)) return hipErrorInvalidValue;
+  if (a.topk_group > 0 && a.n_group > GATE_MAX_GROUPS) return hipErrorInvalidValue;
+  if (a.T >= GATE_WIDE_FROM)
+    hipLaunchKernelGGL((gate_topk_kernel<GATE_WIDE>), dim3(ceil_div(a.T, GATE_WIDE)), dim3(GATE_WIDE * WAVE), 0, stream, a);
+  else
+    hipLaunchKernelGGL((gate_topk_kernel<1>), dim3(a.T), dim3(WAVE), 0, stream, a);
+  return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------

@@ -128,14 +128,19 @@ def test_route_topk(name, T):
 
 
 @pytest.mark.parametrize("E,n_group,topk_group,k,gate", [
-    (96, 12, 3, 6, "sigmoid"),    # groups of 8 experts: not whole 16-lane slots
-    (64, 4, 2, 4, "softmax"),     # groups of 16: one slot per group
-    (160, 5, 2, 8, "sigmoid"),    # groups of 32 with two unused slots per lane (12 slots launched)
+    (96, 12, 3, 6, "sigmoid"),    # groups of 8 experts: 2 lanes each
+    (64, 4, 2, 4, "softmax"),     # groups of 16: 4 lanes each
+    (160, 5, 2, 8, "sigmoid"),    # groups of 32: 8 lanes each, 24 lanes past E
+    (96, 8, 3, 6, "sigmoid"),     # groups of 12: 3 lanes, not a power of two
+    (90, 15, 4, 8, "softmax"),    # groups of 6: not whole lanes
+    (256, 2, 1, 8, "sigmoid"),    # groups of 128: 32 lanes, across rows of 16
+    (64, 32, 6, 8, "sigmoid"),    # groups of 2: half a lane, 32 groups
 ])
 def test_route_group_limited_shapes(E, n_group, topk_group, k, gate):
-    """Group-limited selection over group sizes that do and do not fill whole
-    16-lane slots (the gate scores groups in one pass over the slots only in
-    the second case)."""
+    """Group-limited selection over group sizes that are and are not whole
+    blocks of at most 16 lanes (4 experts per lane): the gate scores groups
+    inside their own lanes in the first case, one group at a time over the
+    wavefront otherwise."""
     L, DeviceLayer, to_device = _L()
     cfg = MoEConfig(name="groups", T=200, d=256, E=E, k=k, gate=gate, n_group=n_group, topk_group=topk_group,
                     dtype="bf16")
@@ -150,23 +155,59 @@ def test_route_group_limited_shapes(E, n_group, topk_group, k, gate):
     assert amb.mean() < 0.05
 
 
-def test_route_exact_ties_go_to_lower_id():
+@pytest.mark.parametrize("E,n_group,per_group_k,gate", [
+    (64, 8, 2, "softmax"),     # groups of 8 (2 lanes): two quota rounds side by side
+    (128, 16, 1, "sigmoid"),   # groups of 8, 16 groups
+    (96, 4, 3, "sigmoid"),     # groups of 24: 6 lanes, not a power of two
+    (60, 10, 1, "softmax"),    # groups of 6: not whole lanes
+    (256, 2, 4, "sigmoid"),    # groups of 128: 32 lanes
+])
+def test_route_per_group_quota_shapes(E, n_group, per_group_k, gate):
+    """Per-group quota selection (per_group_k from every group) over group
+    sizes that are and are not whole blocks of at most 16 lanes: the groups'
+    rounds run side by side in the first case, one group at a time
+    otherwise."""
+    L, DeviceLayer, to_device = _L()
+    cfg = MoEConfig(name="quota", T=200, d=256, E=E, k=n_group * per_group_k, gate=gate, n_group=n_group,
+                    per_group_k=per_group_k, dtype="bf16")
+    inp = make_inputs(cfg)
+    U.say(f"[gpu] route quota E={E} groups={n_group} per_group_k={per_group_k} {gate}")
+    lay = DeviceLayer(cfg, inp)
+    idx, w = lay.route_topk()
+    torch.cuda.synchronize()
+    ref = dict(zip(("z", "scores", "idx", "w"), O.route(inp, cfg)))
+    amb = U.compare_routing(cfg, ref, U.np_of(idx), U.np_of(w), U.x64_of(inp),
+                            inp["w_router"].astype(np.float64))
+    assert amb.mean() < 0.05
+
+
+TIE_CASES = [
+    # plain top-k: twins in different lanes and (21, 23) in one lane
+    (dict(E=32, k=6), ((3, 17), (9, 30), (5, 12), (21, 23))),
+    # per-group quota, groups of 8: twins in one lane (17, 19), in the two
+    # lanes of one group (40, 45) and (3, 6)
+    (dict(E=64, k=16, n_group=8, per_group_k=2), ((17, 19), (40, 45), (3, 6))),
+]
+
+
+@pytest.mark.parametrize("case", range(len(TIE_CASES)))
+def test_route_exact_ties_go_to_lower_id(case):
     """Duplicated router columns give bit-identical logits on both sides; the
     lower expert id must win every such tie."""
     L, DeviceLayer, to_device = _L()
+    shape, twins = TIE_CASES[case]
     for gate in ("softmax", "sigmoid"):
-        cfg = MoEConfig(name="ties", T=96, d=256, E=32, k=6, gate=gate, dtype="bf16")
+        cfg = MoEConfig(name="ties", T=96, d=256, gate=gate, dtype="bf16", **shape)
         inp = make_inputs(cfg)
         wr = inp["w_router"]
-        wr[:, 17] = wr[:, 3]
-        wr[:, 30] = wr[:, 9]
-        wr[:, 12] = wr[:, 5]
-        U.say(f"[gpu] exact ties {gate}")
+        for a, b in twins:
+            wr[:, b] = wr[:, a]
+        U.say(f"[gpu] exact ties {shape} {gate}")
         lay = DeviceLayer(cfg, inp)
         idx, w = lay.route_topk()
         ref = dict(zip(("z", "scores", "idx", "w"), O.route(inp, cfg)))
         got = U.np_of(idx)
-        for a, b in ((3, 17), (9, 30), (5, 12)):
+        for a, b in twins:
             # whenever both twins are chosen the lower id comes first; when only
             # one is chosen it is the lower id
             for t in range(cfg.T):
