@@ -517,7 +517,13 @@ def test_grouped_ffn_shared(name):
 # ----------------------------------------------------------------------------
 # combine on given rows
 # ----------------------------------------------------------------------------
-@pytest.mark.parametrize("name", ["tiny_fp32", "longcat_zero_bf16"])
+# 1088 columns over 37 tokens: a thread's second 1024-column pass holds
+# only a 64-column tail
+COMBINE_RAGGED = MoEConfig(name="combine_cols", T=37, d=1088, E=16, k=4, gate="softmax", ffn_begin=0, n_ffn=8,
+                           zero_begin=8, n_zero=4, inter=64, dtype="bf16")
+
+
+@pytest.mark.parametrize("name", ["tiny_fp32", "longcat_zero_bf16", "combine_cols"])
 @pytest.mark.parametrize("with_shared", [False, True])
 def test_combine(name, with_shared):
     """moe_combine on given expert rows (random), its own routing tables, and
@@ -525,8 +531,13 @@ def test_combine(name, with_shared):
     weighted rows of resident experts + the weighted x of identity experts,
     against the same sum written out in fp64."""
     L, DeviceLayer, to_device = _L()
-    cfg, inp = U.inputs(name)
-    lay = U.device_layer(name)
+    if name == COMBINE_RAGGED.name:
+        cfg = COMBINE_RAGGED
+        inp = make_inputs(cfg)
+        lay = DeviceLayer(cfg, inp)
+    else:
+        cfg, inp = U.inputs(name)
+        lay = U.device_layer(name)
     idx, w = make_routing(cfg, seed=21)
     rng = np.random.default_rng(22)
     R = cfg.T * cfg.k
