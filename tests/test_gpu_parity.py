@@ -844,6 +844,25 @@ def test_w8a8_integer_products_exact(T, E, k, inter):
     U.record(test="w8a8_integer_products_exact", T=T, max_abs_accumulator=max_acc)
 
 
+@pytest.mark.parametrize("T,d,inter", [(33, 8256, 64), (17, 1088, 320), (5, 64, 6208)])
+def test_w8a8_code_shapes(T, d, inter):
+    """Row quantisation over row lengths that leave part of a wavefront's
+    columns empty (64: a quarter of one load; 1088, 320: a partial second
+    load), that need several 8192-column passes (8256) or a wide register
+    set (6208), and a zero row (token 0: x = 0, so its h row is 0 too): codes
+    and scales of x and h bit-exact, the products as in the full-layer test."""
+    L, DeviceLayer, to_device = _L()
+    cfg = MoEConfig(name="w8codes", T=T, d=d, E=4, k=2, gate="softmax", n_ffn=4, inter=inter, dtype="w8a8")
+    inp = make_inputs(cfg, seed=4)
+    inp["x"][0] = 0
+    lay = DeviceLayer(cfg, inp)
+    U.say(f"[gpu] W8A8 code shapes T={T} d={d} inter={inter}")
+    _, t = lay.layer_with_tables(intermediates=True)
+    torch.cuda.synchronize()
+    assert float(U.np_of(t["s_x"])[0]) == 0.0 and not U.np_of(t["q_x"])[0].any()
+    _check_w8a8_integer_products(cfg, inp, t, silu_exact=False)
+
+
 def _bits(t):
     return t.view(torch.int16) if t.dtype == torch.bfloat16 else t
 
