@@ -188,11 +188,18 @@ typedef struct moe_tuning {
      *  - big_min_rows: bf16 experts with at least this many rows take the
      *    256-row tiles (default 256).
      *  - dense_big_rows: bf16 dense products (the shared expert) of at least
-     *    this many rows take the 256-row tiles (default 2048). */
+     *    this many rows take the 256-row tiles (default 2048).
+     *  - decode_tile_rows: below prefill_tokens, the height of the routed
+     *    experts' tiles, 64 (default) or 32; any other nonzero value is
+     *    MOE_ERR_INVALID_ARG. 32-row tiles halve the padded matrix-core rows
+     *    of experts with at most 32 rows; an expert with more takes several
+     *    tiles, each reading its weights again, so the choice belongs to a
+     *    load bucket whose largest expert fits one tile. */
     int32_t prefill_tokens;
     int32_t stream_max_rows;
     int32_t big_min_rows;
     int32_t dense_big_rows;
+    int32_t decode_tile_rows;
 } moe_tuning;
 
 /*

@@ -92,6 +92,8 @@ struct TilePolicy {
   // below the prefill threshold: experts with at most this many rows go to
   // the 32-row weight-streaming kernel (0: none; only a caller's theta)
   int decode_stream_rows = 0;
+  // below the prefill threshold: the routed experts' tile height (64 or 32)
+  int decode_tile_rows = 64;
 };
 TilePolicy policy_of(const moe_tuning& t) {
   TilePolicy p;
@@ -99,6 +101,7 @@ TilePolicy policy_of(const moe_tuning& t) {
   if (t.stream_max_rows > 0) p.stream_max_rows = p.decode_stream_rows = t.stream_max_rows;
   if (t.big_min_rows > 0) p.big_min_rows = t.big_min_rows;
   if (t.dense_big_rows > 0) p.dense_big_rows = t.dense_big_rows;
+  if (t.decode_tile_rows > 0) p.decode_tile_rows = t.decode_tile_rows;
   return p;
 }
 
@@ -394,7 +397,7 @@ moe_status run_routed(GemmArgs g, const moe_desc* d, GemmElem el, int planes, Ge
     L.partial = partial;
     L.part_rows = r_max(d);
     L.max_wgs = capped_wgs(cap, splits);
-    L.tile_rows = 64;
+    L.tile_rows = pol.decode_tile_rows;
     L.min_rows = pol.decode_stream_rows + 1;
     L.max_rows = INT32_MAX;
     g.tiles_y = ceil_div(r_max(d), L.tile_rows) + g.n_groups;
@@ -408,7 +411,7 @@ moe_status run_routed(GemmArgs g, const moe_desc* d, GemmElem el, int planes, Ge
     L.partial = partial;
     L.part_rows = r_max(d);
     L.max_wgs = capped_wgs(cap, splits);
-    L.tile_rows = 64;
+    L.tile_rows = pol.decode_tile_rows;
     L.min_rows = 1;
     L.max_rows = INT32_MAX;
     g.tiles_y = ceil_div(r_max(d), L.tile_rows) + g.n_groups;
@@ -422,7 +425,7 @@ moe_status run_routed(GemmArgs g, const moe_desc* d, GemmElem el, int planes, Ge
     L.splits = 1;
     L.part_rows = r_max(d);
     L.max_wgs = capped_wgs(cap, 1);
-    L.tile_rows = 64;
+    L.tile_rows = prefill ? 64 : pol.decode_tile_rows;
     L.min_rows = 1;
     L.max_rows = INT32_MAX;
     g.tiles_y = ceil_div(r_max(d), L.tile_rows) + g.n_groups;
@@ -859,7 +862,8 @@ moe_status moe_layer(const moe_desc* d, const moe_weights* w, const void* x, voi
     if (aux->stream2 && aux->stream2 == stream) return MOE_ERR_INVALID_ARG;
     const moe_tuning* t = aux->tuning;
     if (t && (t->shared_ffn1_wgs < 0 || t->shared_ffn2_wgs < 0 || t->routed_ffn1_wgs < 0 || t->routed_ffn2_wgs < 0 ||
-              t->prefill_tokens < 0 || t->stream_max_rows < 0 || t->big_min_rows < 0 || t->dense_big_rows < 0))
+              t->prefill_tokens < 0 || t->stream_max_rows < 0 || t->big_min_rows < 0 || t->dense_big_rows < 0 ||
+              (t->decode_tile_rows != 0 && t->decode_tile_rows != 32 && t->decode_tile_rows != 64)))
       return MOE_ERR_INVALID_ARG;
   }
   const size_t need = ws_bytes_of(d, MOE_OP_LAYER);

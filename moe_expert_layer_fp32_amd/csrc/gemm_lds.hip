@@ -380,10 +380,12 @@ __device__ __forceinline__ void gemm_lds_tile(const GemmArgs& a, const LdsArgs& 
 #ifndef MOE_RING_S2_BM64
 #define MOE_RING_S2_BM64 4
 #endif
+// 32-row tiles (one row block) hold half the accumulators of 64-row ones:
+// an 8-step ring at two wavefronts per SIMD fits their registers.
 template <class Tr, int S, int EPI, int NF, int BM>
-constexpr int ring_steps() { return S == 1 || BM == 128 ? 8 : MOE_RING_S2_BM64; }
+constexpr int ring_steps() { return S == 1 || BM == 128 || BM == 32 ? 8 : MOE_RING_S2_BM64; }
 template <class Tr, int S, int EPI, int NF, int BM>
-constexpr int lds_waves_per_eu() { return BM == 64 && NF == 32 && ring_steps<Tr, S, EPI, NF, BM>() <= 8 ? 2 : 1; }
+constexpr int lds_waves_per_eu() { return BM <= 64 && NF == 32 && ring_steps<Tr, S, EPI, NF, BM>() <= 8 ? 2 : 1; }
 
 template <class Tr, int S, int EPI, int NF, int BM>
 __global__ __launch_bounds__(WG_THREADS) __attribute__((amdgpu_waves_per_eu(lds_waves_per_eu<Tr, S, EPI, NF, BM>())))
@@ -557,6 +559,7 @@ static hipError_t launch_lds_shape(const GemmArgs& a, const LdsArgs& L, hipStrea
       return L.tile_rows == 64 ? launch_lds_one<Tr, S, EPI, 64, 64>(a, L, stream, ev)
                                : launch_lds_one<Tr, S, EPI, 64, 128>(a, L, stream, ev);
   }
+  if (L.tile_rows == 32) return launch_lds_one<Tr, S, EPI, 32, 32>(a, L, stream, ev);
   return L.tile_rows == 64 ? launch_lds_one<Tr, S, EPI, 32, 64>(a, L, stream, ev)
                            : launch_lds_one<Tr, S, EPI, 32, 128>(a, L, stream, ev);
 }

@@ -60,7 +60,8 @@ class MoeTuning(ctypes.Structure):
     _fields_ = [("shared_ffn1_wgs", ctypes.c_int32), ("shared_ffn2_wgs", ctypes.c_int32),
                 ("routed_ffn1_wgs", ctypes.c_int32), ("routed_ffn2_wgs", ctypes.c_int32),
                 ("prefill_tokens", ctypes.c_int32), ("stream_max_rows", ctypes.c_int32),
-                ("big_min_rows", ctypes.c_int32), ("dense_big_rows", ctypes.c_int32)]
+                ("big_min_rows", ctypes.c_int32), ("dense_big_rows", ctypes.c_int32),
+                ("decode_tile_rows", ctypes.c_int32)]
 
 
 class MoeAux(ctypes.Structure):

@@ -5,7 +5,8 @@ VOL.12ï¼šæ˜‡è…¾Ã—ç›˜å¤", section SwiftGMMï¼šä¸“å®¶è®¡ç®—çªå‡»é˜Ÿï¼Œé—ªç”µé€Ÿåº
 tile parameters are predicted from past loads instead of being fixed. Here
 the parameters are the members of moe_tuning: the tile choice by per-expert
 row count (the prefill threshold, theta of the weight-streaming class, the
-256-row classes of experts and of dense products) and the workgroup caps of
+256-row classes of experts and of dense products, the decode tile height)
+and the workgroup caps of
 each product. For one layer shape, stream count and bucket of its
 per-expert token counts, a few candidates are timed on the caller's own
 layer calls and the fastest is kept in a host-side table. The table is keyed
@@ -36,7 +37,7 @@ from . import lib as L
 TABLE_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "tuning_table.json")
 
 FIELDS = ("shared_ffn1_wgs", "shared_ffn2_wgs", "routed_ffn1_wgs", "routed_ffn2_wgs",
-          "prefill_tokens", "stream_max_rows", "big_min_rows", "dense_big_rows")
+          "prefill_tokens", "stream_max_rows", "big_min_rows", "dense_big_rows", "decode_tile_rows")
 
 # Candidate caps (shared gate/up, shared down); (0, 0) is the library's own
 # choice and always a candidate.
@@ -46,8 +47,9 @@ NO_BIG = 1 << 30          # a big_min_rows / dense_big_rows no layer reaches: 25
 
 def candidates_for(desc: L.MoeDesc, streams: int) -> list[dict]:
     """Candidate limits for one layer shape. Decode sizes (below the default
-    prefill threshold of 1024 tokens): the shared expert's caps, and the
-    per-expert tile classes of the prefill regime applied early. Prefill
+    prefill threshold of 1024 tokens): the shared expert's caps, the
+    per-expert tile classes of the prefill regime applied early, and 32-row
+    tiles for the routed experts (with and without the widest caps). Prefill
     sizes: caps of the shared products and of the routed gate/up, with and
     without 256-row tiles for routed experts."""
     out = []
@@ -62,6 +64,8 @@ def candidates_for(desc: L.MoeDesc, streams: int) -> list[dict]:
             out.append(limits(stream_max_rows=theta))
             if best_caps != (0, 0):
                 out.append(limits(best_caps[0], best_caps[1], stream_max_rows=theta))
+        for c in shared:            # 32-row tiles for the routed experts
+            out.append(limits(c[0], c[1], decode_tile_rows=32))
         return out
     shared = ((0, 0), (128, 128), (192, 192)) if (has_shared and streams == 2) else ((0, 0),)
     routed = ((0, 0), (160, 0)) if streams == 2 else ((0, 0),)
@@ -73,13 +77,13 @@ def candidates_for(desc: L.MoeDesc, streams: int) -> list[dict]:
 
 
 def limits(shared_ffn1_wgs=0, shared_ffn2_wgs=0, routed_ffn1_wgs=0, routed_ffn2_wgs=0, prefill_tokens=0,
-           stream_max_rows=0, big_min_rows=0, dense_big_rows=0) -> dict:
+           stream_max_rows=0, big_min_rows=0, dense_big_rows=0, decode_tile_rows=0) -> dict:
     return dict(zip(FIELDS, (shared_ffn1_wgs, shared_ffn2_wgs, routed_ffn1_wgs, routed_ffn2_wgs, prefill_tokens,
-                             stream_max_rows, big_min_rows, dense_big_rows)))
+                             stream_max_rows, big_min_rows, dense_big_rows, decode_tile_rows)))
 
 
 def label(lim: dict) -> str:
-    """Short name of a limits dict: the four caps in FIELDS order."""
+    """Short name of a limits dict: its members in FIELDS order."""
     return "/".join(str(int(lim.get(f, 0))) for f in FIELDS)
 
 

@@ -171,10 +171,17 @@ def test_negative_launch_limit_rejected(L):
         aux = L.MoeAux(tuning=ctypes.pointer(t))
         assert lib.moe_layer(ctypes.byref(d), ctypes.byref(w), FAKE, FAKE, ctypes.byref(aux), FAKE, 1 << 40,
                              None) == -1, field
+    # a decode tile height other than 32 or 64
+    for rows in (-1, 16, 48, 128):
+        t = L.MoeTuning(decode_tile_rows=rows)
+        aux = L.MoeAux(tuning=ctypes.pointer(t))
+        assert lib.moe_layer(ctypes.byref(d), ctypes.byref(w), FAKE, FAKE, ctypes.byref(aux), FAKE, 1 << 40,
+                             None) == -1, rows
     # zero and positive limits pass validation; only the workspace check fails
-    t = L.MoeTuning(shared_ffn1_wgs=128, routed_ffn2_wgs=0)
-    aux = L.MoeAux(tuning=ctypes.pointer(t))
-    assert lib.moe_layer(ctypes.byref(d), ctypes.byref(w), FAKE, FAKE, ctypes.byref(aux), FAKE, 0, None) == -3
+    for t in (L.MoeTuning(shared_ffn1_wgs=128, routed_ffn2_wgs=0), L.MoeTuning(decode_tile_rows=32),
+              L.MoeTuning(decode_tile_rows=64)):
+        aux = L.MoeAux(tuning=ctypes.pointer(t))
+        assert lib.moe_layer(ctypes.byref(d), ctypes.byref(w), FAKE, FAKE, ctypes.byref(aux), FAKE, 0, None) == -3
 
 
 def test_pack_rejects_small_destination(L):

@@ -1026,6 +1026,31 @@ def test_layer_decode_stream_theta(name, theta):
         assert torch.equal(_bits(y), _bits(y2))
 
 
+@pytest.mark.parametrize("name,extra", [("dsv3_decode_share_bf16", {}), ("longcat_zero_bf16", {}),
+                                        ("pangu_moge_w8a8", {}), ("tiny_fp32", {}),
+                                        ("longcat_zero_bf16", {"stream_max_rows": 20}),
+                                        ("dsv3_decode_share_bf16", {"shared_ffn1_wgs": 128})])
+def test_layer_decode_tile_rows_32(name, extra):
+    """Decode workloads on 32-row routed tiles (moe_tuning.decode_tile_rows):
+    experts of at most 32 rows (DeepSeek-style share, split reduction) take
+    one tile, larger ones several (LongCat-style, W8A8 with its int8 path,
+    fp32); also beside a caller's theta and under a shared cap. Against the
+    oracle, and equal to the 64-row call up to fp32 summation order."""
+    L, DeviceLayer, to_device = _L()
+    from moe_expert_layer_fp32_amd.layer import SecondStream
+    from moe_expert_layer_fp32_amd import tuning as TU
+    cfg, inp = U.inputs(name)
+    lay = U.device_layer(name)
+    t = TU.to_struct(TU.limits(decode_tile_rows=32, **extra))
+    U.say(f"[gpu] layer {name} 32-row decode tiles {extra}")
+    second = SecondStream() if cfg.shared_inter else None
+    y = _check_layer(cfg, inp, lay, second=second, tuning=t)
+    y0 = lay.layer(second=second)
+    torch.cuda.synchronize()
+    _, dev = U.output_errors(U.np_of(y), U.np_of(y0).astype(np.float64), cfg.dtype)
+    U.record(test="layer_decode_tile_rows_32", cfg=name, extra=extra, err_vs_64_rows=dev)
+
+
 def test_layer_largest_k_group_limited():
     """k = 16 (the largest built), group-limited selection of 4 of 8 groups
     over 256 experts, 16 resident, two streams."""

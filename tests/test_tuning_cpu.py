@@ -43,7 +43,9 @@ def test_library_choice_is_no_struct(TU):
     assert TU.to_struct(TU.limits()) is None
     t = TU.to_struct(TU.limits(96, 0, 8, 0))
     assert (t.shared_ffn1_wgs, t.shared_ffn2_wgs, t.routed_ffn1_wgs, t.routed_ffn2_wgs) == (96, 0, 8, 0)
-    assert TU.label(TU.limits(96, 0, 8, 0)) == "96/0/8/0/0/0/0/0"
+    assert TU.label(TU.limits(96, 0, 8, 0)) == "96/0/8/0/0/0/0/0/0"
+    t = TU.to_struct(TU.limits(decode_tile_rows=32))
+    assert t.decode_tile_rows == 32 and TU.label(TU.limits(decode_tile_rows=32)) == "0/0/0/0/0/0/0/0/32"
 
 
 def test_load_bucket_and_key(TU):
@@ -76,6 +78,8 @@ def test_candidates_by_regime(TU):
             assert set(c) == set(TU.FIELDS) and all(v >= 0 for v in c.values())
             TU.to_struct(c)
     assert any(c["prefill_tokens"] == dec.T for c in TU.candidates_for(dec, 2))
+    assert any(c["decode_tile_rows"] == 32 for c in TU.candidates_for(dec, 2))
+    assert not any(c["decode_tile_rows"] for c in TU.candidates_for(pre, 2))
     pre2 = TU.candidates_for(pre, 2)
     assert any(c["big_min_rows"] == TU.NO_BIG for c in pre2)
     assert any(c["routed_ffn1_wgs"] > 0 for c in pre2) and any(c["shared_ffn1_wgs"] > 0 for c in pre2)
