@@ -315,8 +315,8 @@ def selection_margins(z: np.ndarray, scores: np.ndarray, cfg):
     k selected experts and the best unselected candidate (the quantity a
     reordering or a swap at the k boundary needs to cross). The second is the
     gap between the last kept and the first dropped group score (inf when no
-    groups are limited). Used by tests to exclude tokens whose choice is within
-    rounding of a tie.
+    groups are limited). A lone candidate (E = 1) has no gap: inf. Used by
+    tests to exclude tokens whose choice is within rounding of a tie.
     """
     T = z.shape[0]
     mz = np.full(T, np.inf)
@@ -330,7 +330,8 @@ def selection_margins(z: np.ndarray, scores: np.ndarray, cfg):
                 members = sorted(range(g * gsize, (g + 1) * gsize), key=lambda e: (-zt[e], e))
                 take = members[: cfg.per_group_k + 1]
                 vals = [zt[e] for e in take]
-                mz[t] = min(mz[t], min(vals[i] - vals[i + 1] for i in range(len(vals) - 1)))
+                if len(vals) > 1:   # a lone member has no boundary to cross
+                    mz[t] = min(mz[t], min(vals[i] - vals[i + 1] for i in range(len(vals) - 1)))
                 sel += members[: cfg.per_group_k]
             v = sorted((zt[e] for e in sel), reverse=True)
             if len(v) > 1:
@@ -346,5 +347,6 @@ def selection_margins(z: np.ndarray, scores: np.ndarray, cfg):
             kept = kept[: cfg.topk_group]
             cand = [e for g in kept for e in range(g * gsize, (g + 1) * gsize)]
         v = sorted((zt[e] for e in cand), reverse=True)[: cfg.k + 1]
-        mz[t] = min(v[i] - v[i + 1] for i in range(len(v) - 1))
+        if len(v) > 1:   # one candidate (E = 1): no order or swap to cross
+            mz[t] = min(v[i] - v[i + 1] for i in range(len(v) - 1))
     return mz, mg

@@ -127,6 +127,25 @@ def test_route_topk(name, T):
     assert amb.mean() < 0.05
 
 
+@pytest.mark.parametrize("E,k,gate", [(1, 1, "softmax"), (2, 2, "sigmoid"), (3, 2, "softmax"), (5, 4, "sigmoid"),
+                                      (255, 16, "softmax")])
+def test_route_expert_counts(E, k, gate):
+    """Plain top-k over expert counts that leave lanes and slots of the
+    gate's wavefront empty (4 experts per lane: E 1, 2, 3, 5) or one slot
+    short of all 256 (E 255, the largest k)."""
+    L, DeviceLayer, to_device = _L()
+    cfg = MoEConfig(name="expert_counts", T=70, d=128, E=E, k=k, gate=gate, n_ffn=min(E, 4), inter=64, dtype="bf16")
+    inp = make_inputs(cfg)
+    U.say(f"[gpu] route E={E} k={k} {gate}")
+    lay = DeviceLayer(cfg, inp)
+    idx, w = lay.route_topk()
+    torch.cuda.synchronize()
+    ref = dict(zip(("z", "scores", "idx", "w"), O.route(inp, cfg)))
+    amb = U.compare_routing(cfg, ref, U.np_of(idx), U.np_of(w), U.x64_of(inp),
+                            inp["w_router"].astype(np.float64))
+    assert amb.mean() < 0.05
+
+
 @pytest.mark.parametrize("E,n_group,topk_group,k,gate", [
     (96, 12, 3, 6, "sigmoid"),    # groups of 8 experts: 2 lanes each
     (64, 4, 2, 4, "softmax"),     # groups of 16: 4 lanes each

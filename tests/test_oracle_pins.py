@@ -181,6 +181,20 @@ def test_selection_margin_is_zero_on_exact_ties():
     assert np.isclose(mz[0], 0.1)
 
 
+def test_selection_margin_of_a_lone_candidate_is_infinite():
+    """One expert (E = 1), or groups of one expert with a quota of one: no
+    other candidate, so no order or swap can be decided by rounding."""
+    z = np.array([[0.7], [-2.0]])
+    mz, mg = O.selection_margins(z, O.gate_scores(z, "softmax"), MoEConfig(name="m", T=2, d=1, E=1, k=1,
+                                                                           gate="softmax"))
+    assert np.all(np.isinf(mz)) and np.all(np.isinf(mg))
+    z = np.array([[0.3, 0.9, 0.1]])
+    cfg = MoEConfig(name="m", T=1, d=1, E=3, k=3, gate="sigmoid", n_group=3, per_group_k=1)
+    mz, _ = O.selection_margins(z, O.gate_scores(z, "sigmoid"), cfg)
+    # only the final order of the three chosen remains: 0.9 - 0.3 and 0.3 - 0.1
+    assert np.isclose(mz[0], 0.2)
+
+
 def test_round_output_bf16_nearest_even():
     vals = np.array([1.0, 1.0 + 2 ** -8, 1.0 + 3 * 2 ** -8, -3.0 - 2 ** -7, 1e-3])
     got = O.round_output(vals, "bf16")
