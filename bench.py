@@ -18,7 +18,9 @@ launch / its mean duration), for the decode workloads the routed experts'
 gate/up projection with SwiGLU (HBM bound: algorithmic bytes per launch / its
 mean duration). Durations come from HIP events stamped by the launch's own
 dispatch on the stream it runs on. `layer_roofline` applies the same roofline
-to the whole call.
+to the whole call. With the default workload the line also carries
+`decode_workloads`: the three decode workloads, each timed the same way by
+this script in a child process (`--no-decode` skips them).
 """
 from __future__ import annotations
 
@@ -27,6 +29,7 @@ import ctypes
 import hashlib
 import json
 import os
+import subprocess
 import sys
 import time
 
@@ -71,6 +74,8 @@ def parse():
                    help="also time the same calls replayed from one captured HIP graph (graph_replay)")
     p.add_argument("--streams", type=int, default=2, choices=(1, 2),
                    help="2: the shared expert runs on a second stream (when the workload has one)")
+    p.add_argument("--no-decode", action="store_true",
+                   help="with the default workload: skip the decode workloads' lines (decode_workloads)")
     p.add_argument("--copy-calibration", action="store_true",
                    help="only run 5 device copies of 1 GiB (the known-size kernel for counter calibration)")
     p.add_argument("--traffic", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "CAL_FETCH_CSV", "CAL_WRITE_CSV"),
@@ -572,8 +577,44 @@ def main() -> int:
         rec["tuning"] = tuned
     if graph is not None:
         rec["graph_replay"] = graph
+    if args.config == DEFAULT_CONFIG and not args.no_decode and not args.limits:
+        rec["decode_workloads"] = decode_lines(args)
     print(json.dumps(rec), flush=True)
     return 0
+
+
+DECODE_CONFIGS = ("longcat_zero_bf16", "dsv3_decode_share_bf16", "pangu_moge_w8a8")
+
+
+def decode_lines(args) -> dict:
+    """The decode workloads, each timed by this script in a child process
+    (same steps and warm-up, tuned table, no CPU baseline): calls per second
+    as tokens/s, the call time, the dominant launch's and the whole call's HBM
+    roofline. A child that fails leaves its exit status instead."""
+    out = {}
+    for name in DECODE_CONFIGS:
+        cmd = [sys.executable, os.path.abspath(__file__), "--config", name, "--steps", str(args.steps),
+               "--warmup", str(args.warmup), "--no-cpu-baseline", "--no-ceiling", "--no-decode"]
+        if args.no_tune:
+            cmd.append("--no-tune")
+        try:
+            r = subprocess.run(cmd, capture_output=True, text=True, timeout=600)
+        except subprocess.TimeoutExpired:
+            out[name] = {"error": "timed out"}
+            continue
+        lines = [l for l in r.stdout.splitlines() if l.startswith("{")]
+        if r.returncode != 0 or not lines:
+            out[name] = {"error": f"exit status {r.returncode}"}
+            continue
+        b = json.loads(lines[-1])
+        roof, lay = b["roofline"], b["layer_roofline"]
+        out[name] = {"value": b["value"], "unit": b["unit"], "ms_per_step": b["ms_per_step"],
+                     "dtype": b["dtype"], "config": b["config"],
+                     "roofline": {k: roof.get(k) for k in ("bound", "achieved", "peak", "unit", "frac", "kernel",
+                                                           "mean_us", "traffic")},
+                     "layer_roofline": {k: lay.get(k) for k in ("bound", "achieved", "peak", "unit", "frac")},
+                     "tuning": (b.get("tuning") or {}).get("limits")}
+    return out
 
 
 if __name__ == "__main__":
