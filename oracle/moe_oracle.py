@@ -315,8 +315,9 @@ def selection_margins(z: np.ndarray, scores: np.ndarray, cfg):
     k selected experts and the best unselected candidate (the quantity a
     reordering or a swap at the k boundary needs to cross). The second is the
     gap between the last kept and the first dropped group score (inf when no
-    groups are limited). A lone candidate (E = 1) has no gap: inf. Used by
-    tests to exclude tokens whose choice is within rounding of a tie.
+    groups are limited, or when every group is kept). A lone candidate
+    (E = 1) has no gap: inf. Used by tests to exclude tokens whose choice is
+    within rounding of a tie.
     """
     T = z.shape[0]
     mz = np.full(T, np.inf)
@@ -341,7 +342,8 @@ def selection_margins(z: np.ndarray, scores: np.ndarray, cfg):
         if cfg.topk_group:
             gs = sorted((group_score(scores[t, g * gsize:(g + 1) * gsize]) for g in range(cfg.n_group)),
                         reverse=True)
-            mg[t] = gs[cfg.topk_group - 1] - gs[cfg.topk_group]
+            if cfg.topk_group < cfg.n_group:   # keeping every group drops none: no group boundary
+                mg[t] = gs[cfg.topk_group - 1] - gs[cfg.topk_group]
             kept = sorted(range(cfg.n_group),
                           key=lambda g: (-group_score(scores[t, g * gsize:(g + 1) * gsize]), g))
             kept = kept[: cfg.topk_group]

@@ -1070,6 +1070,68 @@ def test_layer_decode_tile_rows_32(name, extra):
     U.record(test="layer_decode_tile_rows_32", cfg=name, extra=extra, err_vs_64_rows=dev)
 
 
+def _random_config(seed: int) -> MoEConfig:
+    """A seeded layer shape drawn across the descriptor's ranges: the three
+    compute types, both gates, plain / group-limited / per-group-quota
+    selection, identity experts before or after the resident range, with and
+    without a shared expert, token counts from 1 to 513."""
+    r = np.random.default_rng(1000 + seed)
+    dtype = ("f32", "bf16", "w8a8")[seed % 3]
+    gate = ("softmax", "sigmoid")[int(r.integers(2))]
+    E = int(r.choice([4, 6, 8, 12, 16, 24, 32, 48, 64, 96, 128, 160, 256]))
+    mode = int(r.integers(3))     # 0 plain, 1 group-limited, 2 per-group quota
+    divs = [g for g in range(2, min(E, 64) + 1) if E % g == 0]
+    n_group, topk_group, per_group_k = 1, 0, 0
+    if mode == 1:
+        groups = [g for g in divs if E // g >= 2]
+        if groups:
+            n_group = int(r.choice(groups))
+            topk_group = int(r.integers(1, n_group + 1))
+    elif mode == 2:
+        groups = [g for g in divs if g <= 16]
+        if groups:
+            n_group = int(r.choice(groups))
+            per_group_k = int(r.integers(1, min(E // n_group, 16 // n_group) + 1))
+    if per_group_k:
+        k = n_group * per_group_k
+    else:
+        k = int(r.integers(1, min(E, 16, topk_group * (E // n_group) if topk_group else 16) + 1))
+    n_zero = int(r.integers(1, E // 4 + 1)) if E >= 4 and r.random() < 0.4 else 0
+    n_ffn = int(r.integers(1, E - n_zero + 1))
+    if n_zero and r.random() < 0.5:      # identity experts ahead of the resident ones
+        zero_begin = int(r.integers(0, E - n_zero - n_ffn + 1))
+        ffn_begin = zero_begin + n_zero
+    else:
+        ffn_begin = int(r.integers(0, E - n_zero - n_ffn + 1))
+        zero_begin = ffn_begin + n_ffn if n_zero else 0
+    return MoEConfig(name=f"random{seed}", T=int(r.choice([1, 3, 17, 64, 100, 255, 513])),
+                     d=int(r.choice([64, 128, 192, 256, 512, 1024])), E=E, k=k, gate=gate, n_group=n_group,
+                     topk_group=topk_group, per_group_k=per_group_k, ffn_begin=ffn_begin, n_ffn=n_ffn,
+                     zero_begin=zero_begin, n_zero=n_zero, inter=int(r.choice([64, 128, 256, 320, 512])),
+                     shared_inter=int(r.choice([0, 0, 64, 256])), dtype=dtype, seed=seed)
+
+
+@pytest.mark.parametrize("seed", range(60))
+def test_layer_random_shapes(seed):
+    """Seeded random layer shapes against the oracle: one stream; two streams
+    where there is a shared expert; every third seed also on 32-row decode
+    tiles (moe_tuning)."""
+    L, DeviceLayer, to_device = _L()
+    from moe_expert_layer_fp32_amd.layer import SecondStream
+    from moe_expert_layer_fp32_amd import tuning as TU
+    cfg = _random_config(seed)
+    cfg.check()
+    inp = make_inputs(cfg, seed=seed)
+    U.say(f"[gpu] random layer {seed}: {cfg}")
+    lay = DeviceLayer(cfg, inp)
+    y1 = _check_layer(cfg, inp, lay)
+    if cfg.shared_inter:
+        y2 = _check_layer(cfg, inp, lay, second=SecondStream())
+        assert torch.equal(_bits(y1), _bits(y2)), "two streams differ from one"
+    if seed % 3 == 0:
+        _check_layer(cfg, inp, lay, tuning=TU.to_struct(TU.limits(decode_tile_rows=32)))
+
+
 def test_layer_largest_k_group_limited():
     """k = 16 (the largest built), group-limited selection of 4 of 8 groups
     over 256 experts, 16 resident, two streams."""

@@ -195,6 +195,19 @@ def test_selection_margin_of_a_lone_candidate_is_infinite():
     assert np.isclose(mz[0], 0.2)
 
 
+def test_group_margin_when_every_group_is_kept():
+    """topk_group == n_group keeps every group: no group is dropped, so the
+    group gap is +inf, and selection reduces to plain top-k (same ids as with
+    one group)."""
+    z = np.array([[0.9, -0.2, 0.4, 0.1, 0.3, -0.5]])
+    s = O.gate_scores(z, "sigmoid")
+    cfg = MoEConfig(name="m", T=1, d=1, E=6, k=3, gate="sigmoid", n_group=3, topk_group=3)
+    mz, mg = O.selection_margins(z, s, cfg)
+    assert np.isinf(mg[0]) and np.isclose(mz[0], 0.1)   # 0.9, 0.4, 0.3 | 0.1: smallest gap 0.4 - 0.3
+    plain = MoEConfig(name="m", T=1, d=1, E=6, k=3, gate="sigmoid")
+    assert O.select_experts(s, cfg).tolist() == O.select_experts(s, plain).tolist() == [[0, 2, 4]]
+
+
 def test_round_output_bf16_nearest_even():
     vals = np.array([1.0, 1.0 + 2 ** -8, 1.0 + 3 * 2 ** -8, -3.0 - 2 ** -7, 1e-3])
     got = O.round_output(vals, "bf16")
