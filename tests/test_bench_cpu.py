@@ -85,3 +85,40 @@ def test_bench_refuses_more_than_one_gpu():
                        text=True, timeout=120)
     assert r.returncode == 2
     assert "one GPU" in r.stderr
+
+
+def test_decode_lines_summarise_each_child(monkeypatch):
+    """decode_workloads: one child run of bench.py per decode workload, with
+    the parent's steps and warm-up and no nested decode lines; each child's
+    last JSON line is summarised, and a child that fails leaves its exit
+    status instead of failing the parent (no GPU: the child runs are faked)."""
+    import json
+    import subprocess
+    import types
+    bench = _bench()
+    calls = []
+
+    def fake_run(cmd, capture_output, text, timeout):
+        calls.append(cmd)
+        name = cmd[cmd.index("--config") + 1]
+        if name == "pangu_moge_w8a8":
+            return types.SimpleNamespace(returncode=1, stdout="", stderr="boom")
+        line = {"value": 1.0, "unit": "tokens/s", "ms_per_step": 0.5, "dtype": "bf16", "config": {"workload": name},
+                "roofline": {"bound": "hbm", "achieved": 4000.0, "peak": 8000.0, "unit": "GB/s", "frac": 0.5,
+                             "kernel": "k", "mean_us": 10.0, "traffic": None, "extra": 1},
+                "layer_roofline": {"bound": "hbm", "achieved": 3000.0, "peak": 8000.0, "unit": "GB/s",
+                                   "frac": 0.375},
+                "tuning": {"limits": {"decode_tile_rows": 32}}}
+        return types.SimpleNamespace(returncode=0, stdout="progress\n" + json.dumps(line) + "\n", stderr="")
+
+    monkeypatch.setattr(subprocess, "run", fake_run)
+    args = types.SimpleNamespace(steps=7, warmup=3, no_tune=False)
+    out = bench.decode_lines(args)
+    assert list(out) == list(bench.DECODE_CONFIGS)
+    for cmd in calls:
+        assert cmd[cmd.index("--steps") + 1] == "7" and cmd[cmd.index("--warmup") + 1] == "3"
+        assert "--no-decode" in cmd and "--no-cpu-baseline" in cmd
+    assert out["pangu_moge_w8a8"] == {"error": "exit status 1"}
+    ok = out["longcat_zero_bf16"]
+    assert ok["ms_per_step"] == 0.5 and ok["roofline"]["frac"] == 0.5 and "extra" not in ok["roofline"]
+    assert ok["layer_roofline"]["frac"] == 0.375 and ok["tuning"] == {"decode_tile_rows": 32}
