@@ -95,7 +95,7 @@ __global__ __launch_bounds__(PERM_THREADS) void permute_kernel(const int* __rest
   // the expert totals (over all chunks); `before` = slots of expert e in the
   // chunks ahead of this one.
   int total = 0, before = 0;
-  if (threadIdx.x < E) {
+  if (int(threadIdx.x) < E) {
     const int e = threadIdx.x;
     for (int w = 0; w < PERM_WAVES; ++w) {
       const int c = hist[w][e];
@@ -141,8 +141,8 @@ __global__ __launch_bounds__(PERM_THREADS) void permute_kernel(const int* __rest
   }
   if (threadIdx.x == 0) expert_base[0] = 0;
   __syncthreads();
-  if (blockIdx.x == 0 && threadIdx.x <= E) offsets[threadIdx.x] = expert_base[threadIdx.x];
-  if (threadIdx.x < E) {
+  if (blockIdx.x == 0 && int(threadIdx.x) <= E) offsets[threadIdx.x] = expert_base[threadIdx.x];
+  if (int(threadIdx.x) < E) {
     const int e = threadIdx.x;
     for (int w = 0; w < PERM_WAVES; ++w) hist[w][e] += expert_base[e] + before;   // segment start per expert
   }
