@@ -428,7 +428,7 @@ moe_status moe_layer_static(const moe_desc* desc, const moe_weights* w, const vo
 
 /*
  * Measurement helper, not a step of the layer: the practical HBM read
- * ceiling against which the weight-streaming products are judged (the
+ * ceiling against which the weight-streaming products are measured (the
  * pages' decode analysis rests on weight movement being the bound: page
  * "华为技术披露集 VOL.12：昇腾×盘古", section SwiftGMM; page
  * "基于Atlas 900 A3 SuperPoD的LongCat-Flash模型推理性能优化实践", section
