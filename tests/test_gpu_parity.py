@@ -967,29 +967,35 @@ def test_layer_sort_boundary(T):
     assert np.array_equal(U.np_of(t2["sorted_slot"]), np.argsort(flat, kind="stable"))
 
 
-@pytest.mark.parametrize("name,T", [("longcat_zero_bf16", None), ("dsv3_decode_share_bf16", None),
-                                    ("pangu_moge_w8a8", None), ("prefill_zipf_bf16", 2048)])
-def test_layer_graph_replay(name, T):
+@pytest.mark.parametrize("name,T,limits", [("longcat_zero_bf16", None, None), ("dsv3_decode_share_bf16", None, None),
+                                           ("pangu_moge_w8a8", None, None), ("prefill_zipf_bf16", 2048, None),
+                                           ("dsv3_decode_share_bf16", None, {"shared_ffn1_wgs": 128,
+                                                                             "decode_tile_rows": 32})])
+def test_layer_graph_replay(name, T, limits):
     """moe_layer captured into a HIP graph (with the shared expert forked onto
     a second stream inside the capture where there is one) replays to the
     eager result bit for bit; new inputs are copied into the captured input
     buffer between replays, with eager work and synchronisations between.
     W8A8 records ev_join twice on the second stream, prefill sizes ev_fork
-    twice (the small experts' down product on the second stream)."""
+    twice (the small experts' down product on the second stream); the
+    DeepSeek-style call also under its table's limits (capped shared
+    gate/up, 32-row routed tiles)."""
     L, DeviceLayer, to_device = _L()
     from moe_expert_layer_fp32_amd.layer import SecondStream
+    from moe_expert_layer_fp32_amd import tuning as TU
     cfg, inp = U.inputs(name, T)
     lay = U.device_layer(name, T)
     second = SecondStream() if cfg.shared_inter else None
+    t = TU.to_struct(TU.limits(**limits)) if limits else None
     xs = [lay.x.clone(), lay.x.flip(0).contiguous()]
-    eager = [lay.layer(x=xi, second=second) for xi in xs]
+    eager = [lay.layer(x=xi, second=second, tuning=t) for xi in xs]
     torch.cuda.synchronize()
     x_buf, y_buf = xs[0].clone(), torch.empty_like(eager[0])
     ws = lay.workspace(L.OP_LAYER)
-    U.say(f"[gpu] graph capture {name} streams={2 if second else 1}")
+    U.say(f"[gpu] graph capture {name} streams={2 if second else 1} limits={limits}")
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
-        lay.layer(x=x_buf, y=y_buf, ws=ws, second=second)
+        lay.layer(x=x_buf, y=y_buf, ws=ws, second=second, tuning=t)
     torch.cuda.synchronize()
     for rep in range(3):
         for xi, ye in zip(xs, eager):
