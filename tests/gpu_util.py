@@ -158,6 +158,29 @@ def output_errors(y_gpu: np.ndarray, y_ref: np.ndarray, out_dtype: str):
 TOL = {"f32": 1e-5, "bf16": 2e-2, "w8a8": 1e-2}
 
 
+def row_rounding_allowance(cfg, inp, idx: np.ndarray, w: np.ndarray, tokens=None) -> np.ndarray:
+    """Per output element of the bf16 layer: the rounding its expert rows
+    take before the weighted sum (each resident expert's and the shared
+    expert's output row is rounded once to bf16, then summed in fp32), i.e.
+    sum_j |w_tj| * half_ulp(u_tj) + half_ulp(shared_t), from the oracle's
+    rows for the ids given. Identity experts contribute x, which is exact."""
+    X32 = np.asarray(O.x_f32(inp))
+    if tokens is not None:
+        X32 = X32[np.asarray(tokens)]
+    n, k = idx.shape
+    allow = np.zeros((n, cfg.d))
+    for e in np.unique(idx):
+        e = int(e)
+        if O.expert_kind(cfg, e) != "ffn":
+            continue
+        tj = np.argwhere(idx == e)
+        u = O.expert_ffn(inp, cfg, e - cfg.ffn_begin, X32[tj[:, 0]])
+        np.add.at(allow, tj[:, 0], np.abs(w[tj[:, 0], tj[:, 1]])[:, None] * half_ulp(u, "bf16"))
+    if cfg.shared_inter:
+        allow += half_ulp(O.shared_ffn(inp, cfg, X32), "bf16")
+    return allow
+
+
 def h_code_flip_allowance(h32: np.ndarray, sh: np.ndarray, q2: np.ndarray, s2: np.ndarray,
                           eps: float = 1e-4) -> np.ndarray:
     """Per-element allowance for int8 codes of h that sit within eps of a

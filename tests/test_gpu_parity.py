@@ -647,7 +647,13 @@ LAYER_CASES = [("tiny_fp32", None), ("tiny_fp32", 333), ("longcat_zero_bf16", No
                ("dsv3_decode_share_bf16", None), ("dsv3_decode_share_bf16", 129), ("pangu_moge_w8a8", None)]
 
 
-def _check_layer(cfg, inp, lay, tokens=None, ws=None, second=None, tuning=None):
+def _check_layer(cfg, inp, lay, tokens=None, ws=None, second=None, tuning=None, any_shape=False):
+    """moe_layer against the oracle. any_shape (shapes drawn at random, where
+    one token can be a large share of the batch and a few expert rows can
+    make up the output): near-tie tokens may be up to a quarter of the batch
+    (or one token), a batch whose exact output is all zero must come out all
+    zero, and the bf16 layer's allowance also covers the rounding of its
+    expert rows to bf16 before the weighted sum."""
     y, t = lay.layer_with_tables(ws=ws, second=second, tuning=tuning)
     torch.cuda.synchronize()
     idx_gpu, w_gpu = U.np_of(t["topk_idx"]), U.np_of(t["topk_w"])
@@ -655,11 +661,26 @@ def _check_layer(cfg, inp, lay, tokens=None, ws=None, second=None, tuning=None):
     sel = slice(None) if tokens is None else np.asarray(tokens)
     x64 = U.x64_of(inp)[sel]
     amb = U.compare_routing(cfg, ref, idx_gpu[sel], w_gpu[sel], x64, inp["w_router"].astype(np.float64))
-    assert amb.mean() < 0.05
+    if any_shape:
+        assert amb.sum() <= max(1, amb.size // 4), f"{int(amb.sum())} near-tie tokens of {amb.size}"
+    else:
+        assert amb.mean() < 0.05
     clear = ~amb
     y_all = U.np_of(y)[sel]
     y_gpu = y_all[clear]
-    lit, beyond = U.output_errors(y_gpu, ref["y"][clear], cfg.dtype)
+    if any_shape and clear.any() and not np.any(ref["y"][clear]):
+        assert not np.any(y_gpu), "exact output is zero"
+        lit = beyond = 0.0
+    elif any_shape and cfg.dtype == "bf16" and clear.any():
+        tok = np.arange(cfg.T)[sel][clear]
+        rows = U.row_rounding_allowance(cfg, inp, ref["idx"][clear], ref["w"][clear], tokens=tok)
+        ref_c = ref["y"][clear]
+        rms = float(np.sqrt(np.mean(ref_c ** 2)))
+        diff = np.abs(y_gpu - ref_c)
+        allow = U.half_ulp(np.maximum(np.abs(ref_c), np.abs(y_gpu)), cfg.dtype) + rows
+        lit, beyond = float(diff.max() / rms), float(np.maximum(diff - allow, 0).max() / rms)
+    else:
+        lit, beyond = U.output_errors(y_gpu, ref["y"][clear], cfg.dtype)
     # Near-tie tokens: the oracle rerun on the GPU's own ids (downstream on
     # identical top-k indices), weights and outputs compared on every one.
     beyond_amb = 0.0
@@ -672,8 +693,12 @@ def _check_layer(cfg, inp, lay, tokens=None, ws=None, second=None, tuning=None):
         # rms of the whole compared batch, so a handful of tokens is measured
         # on the same scale as the rest
         rms_all = float(np.sqrt(np.mean(ref["y"][clear] ** 2))) if clear.any() else 1.0
+        if any_shape and rms_all == 0.0:
+            rms_all = max(float(np.sqrt(np.mean(ref_amb["y"] ** 2))), 1e-30)
         diff = np.abs(y_all[amb] - ref_amb["y"])
         allow = U.half_ulp(np.maximum(np.abs(ref_amb["y"]), np.abs(y_all[amb])), cfg.dtype)
+        if any_shape and cfg.dtype == "bf16":
+            allow = allow + U.row_rounding_allowance(cfg, inp, idx_gpu[sel][amb], ref_amb["w"], tokens=amb_tok)
         beyond_amb = float(np.maximum(diff - allow, 0).max() / rms_all)
     U.say(f"    {cfg.name} T={cfg.T}: max|err|/rms literal {lit:.3e} beyond-rounding {beyond:.3e} "
           f"near-tie tokens {int(amb.sum())} (their error under identical ids {beyond_amb:.3e})")
@@ -1119,9 +1144,9 @@ def _random_config(seed: int) -> MoEConfig:
 
 @pytest.mark.parametrize("seed", range(60))
 def test_layer_random_shapes(seed):
-    """Seeded random layer shapes against the oracle: one stream; two streams
-    where there is a shared expert; every third seed also on 32-row decode
-    tiles (moe_tuning)."""
+    """Seeded random layer shapes against the oracle (any_shape checks, see
+    _check_layer): one stream; two streams where there is a shared expert;
+    every third seed also on 32-row decode tiles (moe_tuning)."""
     L, DeviceLayer, to_device = _L()
     from moe_expert_layer_fp32_amd.layer import SecondStream
     from moe_expert_layer_fp32_amd import tuning as TU
@@ -1130,12 +1155,12 @@ def test_layer_random_shapes(seed):
     inp = make_inputs(cfg, seed=seed)
     U.say(f"[gpu] random layer {seed}: {cfg}")
     lay = DeviceLayer(cfg, inp)
-    y1 = _check_layer(cfg, inp, lay)
+    y1 = _check_layer(cfg, inp, lay, any_shape=True)
     if cfg.shared_inter:
-        y2 = _check_layer(cfg, inp, lay, second=SecondStream())
+        y2 = _check_layer(cfg, inp, lay, second=SecondStream(), any_shape=True)
         assert torch.equal(_bits(y1), _bits(y2)), "two streams differ from one"
     if seed % 3 == 0:
-        _check_layer(cfg, inp, lay, tuning=TU.to_struct(TU.limits(decode_tile_rows=32)))
+        _check_layer(cfg, inp, lay, tuning=TU.to_struct(TU.limits(decode_tile_rows=32)), any_shape=True)
 
 
 def test_layer_largest_k_group_limited():
