@@ -1101,12 +1101,14 @@ def test_layer_decode_tile_rows_32(name, extra):
     U.record(test="layer_decode_tile_rows_32", cfg=name, extra=extra, err_vs_64_rows=dev)
 
 
-def _random_config(seed: int) -> MoEConfig:
+def _random_config(seed: int, prefill: bool = False) -> MoEConfig:
     """A seeded layer shape drawn across the descriptor's ranges: the three
     compute types, both gates, plain / group-limited / per-group-quota
     selection, identity experts before or after the resident range, with and
-    without a shared expert, token counts from 1 to 513."""
-    r = np.random.default_rng(1000 + seed)
+    without a shared expert, token counts from 1 to 513 (prefill: 1024 to
+    2048, the regime of the per-expert tile classes and, for bf16, 256-row
+    tiles and the two-stream order)."""
+    r = np.random.default_rng(1000 + seed + (100000 if prefill else 0))
     dtype = ("f32", "bf16", "w8a8")[seed % 3]
     gate = ("softmax", "sigmoid")[int(r.integers(2))]
     E = int(r.choice([4, 6, 8, 12, 16, 24, 32, 48, 64, 96, 128, 160, 256]))
@@ -1135,8 +1137,10 @@ def _random_config(seed: int) -> MoEConfig:
     else:
         ffn_begin = int(r.integers(0, E - n_zero - n_ffn + 1))
         zero_begin = ffn_begin + n_ffn if n_zero else 0
-    return MoEConfig(name=f"random{seed}", T=int(r.choice([1, 3, 17, 64, 100, 255, 513])),
-                     d=int(r.choice([64, 128, 192, 256, 512, 1024])), E=E, k=k, gate=gate, n_group=n_group,
+    T = int(r.choice([1024, 1100, 1536, 2048])) if prefill else int(r.choice([1, 3, 17, 64, 100, 255, 513]))
+    d = int(r.choice([64, 128, 256, 512])) if prefill else int(r.choice([64, 128, 192, 256, 512, 1024]))
+    return MoEConfig(name=f"random{'_prefill' if prefill else ''}{seed}", T=T, d=d, E=E, k=k, gate=gate,
+                     n_group=n_group,
                      topk_group=topk_group, per_group_k=per_group_k, ffn_begin=ffn_begin, n_ffn=n_ffn,
                      zero_begin=zero_begin, n_zero=n_zero, inter=int(r.choice([64, 128, 256, 320, 512])),
                      shared_inter=int(r.choice([0, 0, 64, 256])), dtype=dtype, seed=seed)
@@ -1161,6 +1165,23 @@ def test_layer_random_shapes(seed):
         assert torch.equal(_bits(y1), _bits(y2)), "two streams differ from one"
     if seed % 3 == 0:
         _check_layer(cfg, inp, lay, tuning=TU.to_struct(TU.limits(decode_tile_rows=32)), any_shape=True)
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_layer_random_prefill_shapes(seed):
+    """Seeded random shapes at prefill sizes (1024 to 2048 tokens) against
+    the oracle, one stream and, with a shared expert, two."""
+    L, DeviceLayer, to_device = _L()
+    from moe_expert_layer_fp32_amd.layer import SecondStream
+    cfg = _random_config(seed, prefill=True)
+    cfg.check()
+    inp = make_inputs(cfg, seed=seed)
+    U.say(f"[gpu] random prefill layer {seed}: {cfg}")
+    lay = DeviceLayer(cfg, inp)
+    y1 = _check_layer(cfg, inp, lay, any_shape=True)
+    if cfg.shared_inter:
+        y2 = _check_layer(cfg, inp, lay, second=SecondStream(), any_shape=True)
+        assert torch.equal(_bits(y1), _bits(y2)), "two streams differ from one"
 
 
 def test_layer_largest_k_group_limited():
