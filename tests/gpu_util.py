@@ -12,7 +12,7 @@ import numpy as np
 import torch
 
 from moe_inputs import get, make_inputs
-from moe_inputs.gen import x_f32
+from moe_inputs.gen import weight_f32, x_f32
 from oracle import moe_oracle as O
 
 U32 = 2.0 ** -24
@@ -158,12 +158,41 @@ def output_errors(y_gpu: np.ndarray, y_ref: np.ndarray, out_dtype: str):
 TOL = {"f32": 1e-5, "bf16": 2e-2, "w8a8": 1e-2}
 
 
-def row_rounding_allowance(cfg, inp, idx: np.ndarray, w: np.ndarray, tokens=None) -> np.ndarray:
-    """Per output element of the bf16 layer: the rounding its expert rows
-    take before the weighted sum (each resident expert's and the shared
-    expert's output row is rounded once to bf16, then summed in fp32), i.e.
-    sum_j |w_tj| * half_ulp(u_tj) + half_ulp(shared_t), from the oracle's
-    rows for the ids given. Identity experts contribute x, which is exact."""
+def _ffn_allowance(cfg, inp, X32: np.ndarray, e_local=None) -> np.ndarray:
+    """Elementwise bound on how far one FFN's output rows (resident expert
+    e_local, or the shared expert when None) may move under the layer's own
+    intermediate precision, beyond the exact result:
+    - bf16: h stored in bf16 (half an ulp of each h, through |W2|) and the
+      output row rounded once to bf16 (half an ulp of it);
+    - W8A8: int8 codes of h within rounding of a half-integer boundary may
+      take the neighbouring code (h_code_flip_allowance);
+    - fp32: fp32 accumulation of the three products, bounded by n * 2^-24 *
+      sum |terms| (first order), through SwiGLU (|silu'| <= 1.1)."""
+    # the shared expert's arrays are the experts' names with an "s" in front
+    pick = (lambda n: inp["s" + n]) if e_local is None else (lambda n: inp[n][e_local])
+    if cfg.dtype == "w8a8":
+        args = [pick(n) for n in ("w1", "s1", "w3", "s3", "w2", "s2")]
+        _, parts = O.swiglu_w8a8(X32, *args, return_parts=True)
+        return h_code_flip_allowance(parts["h"].astype(np.float32), parts["sh"], args[4], args[5])
+    W1, W3, W2 = (np.asarray(weight_f32(pick(n)), np.float64) for n in ("w1", "w3", "w2"))
+    X = np.asarray(X32, np.float64)
+    a, b = X @ W1, X @ W3
+    sa = O.silu(a)
+    h = sa * b
+    aW2 = np.abs(W2)
+    if cfg.dtype == "bf16":
+        return half_ulp(h, "bf16") @ aW2 + half_ulp(h @ W2, "bf16")
+    u = 2.0 ** -24
+    da = X.shape[1] * u * (np.abs(X) @ np.abs(W1))
+    db = X.shape[1] * u * (np.abs(X) @ np.abs(W3))
+    dh = 1.1 * np.abs(b) * da + np.abs(sa) * db + 4 * u * np.abs(h)
+    return dh @ aW2 + W2.shape[0] * u * (np.abs(h) @ aW2)
+
+
+def layer_allowance(cfg, inp, idx: np.ndarray, w: np.ndarray, tokens=None) -> np.ndarray:
+    """Per output element: sum_j |w_tj| * (the allowance of expert e_tj's row,
+    _ffn_allowance) + the shared expert's, for the ids given. Identity experts
+    contribute x, which is exact; non-resident ones nothing."""
     X32 = np.asarray(O.x_f32(inp))
     if tokens is not None:
         X32 = X32[np.asarray(tokens)]
@@ -174,10 +203,10 @@ def row_rounding_allowance(cfg, inp, idx: np.ndarray, w: np.ndarray, tokens=None
         if O.expert_kind(cfg, e) != "ffn":
             continue
         tj = np.argwhere(idx == e)
-        u = O.expert_ffn(inp, cfg, e - cfg.ffn_begin, X32[tj[:, 0]])
-        np.add.at(allow, tj[:, 0], np.abs(w[tj[:, 0], tj[:, 1]])[:, None] * half_ulp(u, "bf16"))
+        r = _ffn_allowance(cfg, inp, X32[tj[:, 0]], e - cfg.ffn_begin)
+        np.add.at(allow, tj[:, 0], np.abs(w[tj[:, 0], tj[:, 1]])[:, None] * r)
     if cfg.shared_inter:
-        allow += half_ulp(O.shared_ffn(inp, cfg, X32), "bf16")
+        allow += _ffn_allowance(cfg, inp, X32)
     return allow
 
 

@@ -652,8 +652,9 @@ def _check_layer(cfg, inp, lay, tokens=None, ws=None, second=None, tuning=None, 
     one token can be a large share of the batch and a few expert rows can
     make up the output): near-tie tokens may be up to a quarter of the batch
     (or one token), a batch whose exact output is all zero must come out all
-    zero, and the bf16 layer's allowance also covers the rounding of its
-    expert rows to bf16 before the weighted sum."""
+    zero, and the allowance also covers what the layer's intermediate
+    precision may move each expert row (gpu_util.layer_allowance: bf16 h and
+    rows, W8A8 h codes at a rounding boundary, fp32 accumulation)."""
     y, t = lay.layer_with_tables(ws=ws, second=second, tuning=tuning)
     torch.cuda.synchronize()
     idx_gpu, w_gpu = U.np_of(t["topk_idx"]), U.np_of(t["topk_w"])
@@ -671,9 +672,9 @@ def _check_layer(cfg, inp, lay, tokens=None, ws=None, second=None, tuning=None, 
     if any_shape and clear.any() and not np.any(ref["y"][clear]):
         assert not np.any(y_gpu), "exact output is zero"
         lit = beyond = 0.0
-    elif any_shape and cfg.dtype == "bf16" and clear.any():
+    elif any_shape and clear.any():
         tok = np.arange(cfg.T)[sel][clear]
-        rows = U.row_rounding_allowance(cfg, inp, ref["idx"][clear], ref["w"][clear], tokens=tok)
+        rows = U.layer_allowance(cfg, inp, ref["idx"][clear], ref["w"][clear], tokens=tok)
         ref_c = ref["y"][clear]
         rms = float(np.sqrt(np.mean(ref_c ** 2)))
         diff = np.abs(y_gpu - ref_c)
@@ -697,8 +698,8 @@ def _check_layer(cfg, inp, lay, tokens=None, ws=None, second=None, tuning=None, 
             rms_all = max(float(np.sqrt(np.mean(ref_amb["y"] ** 2))), 1e-30)
         diff = np.abs(y_all[amb] - ref_amb["y"])
         allow = U.half_ulp(np.maximum(np.abs(ref_amb["y"]), np.abs(y_all[amb])), cfg.dtype)
-        if any_shape and cfg.dtype == "bf16":
-            allow = allow + U.row_rounding_allowance(cfg, inp, idx_gpu[sel][amb], ref_amb["w"], tokens=amb_tok)
+        if any_shape:
+            allow = allow + U.layer_allowance(cfg, inp, idx_gpu[sel][amb], ref_amb["w"], tokens=amb_tok)
         beyond_amb = float(np.maximum(diff - allow, 0).max() / rms_all)
     U.say(f"    {cfg.name} T={cfg.T}: max|err|/rms literal {lit:.3e} beyond-rounding {beyond:.3e} "
           f"near-tie tokens {int(amb.sum())} (their error under identical ids {beyond_amb:.3e})")
