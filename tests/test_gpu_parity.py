@@ -647,6 +647,9 @@ LAYER_CASES = [("tiny_fp32", None), ("tiny_fp32", 333), ("longcat_zero_bf16", No
                ("dsv3_decode_share_bf16", None), ("dsv3_decode_share_bf16", 129), ("pangu_moge_w8a8", None)]
 
 
+ANY_SHAPE_TOL = 1e-4
+
+
 def _check_layer(cfg, inp, lay, tokens=None, ws=None, second=None, tuning=None, any_shape=False):
     """moe_layer against the oracle. any_shape (shapes drawn at random, where
     one token can be a large share of the batch and a few expert rows can
@@ -706,8 +709,11 @@ def _check_layer(cfg, inp, lay, tokens=None, ws=None, second=None, tuning=None, 
     U.record(test="layer", cfg=cfg.name, T=cfg.T, sampled=None if tokens is None else len(tokens),
              err_literal=lit, err_beyond_rounding=beyond, near_tie_tokens=int(amb.sum()),
              near_tie_err_beyond_rounding=beyond_amb)
-    assert beyond <= U.TOL[cfg.dtype]
-    assert beyond_amb <= U.TOL[cfg.dtype]
+    # any_shape: beyond the allowance the residual is fp32 arithmetic (measured
+    # <= 1.1e-6 of rms over 568 shapes), so the bar is 1e-4 for every dtype
+    tol = min(U.TOL[cfg.dtype], ANY_SHAPE_TOL) if any_shape else U.TOL[cfg.dtype]
+    assert beyond <= tol, f"error beyond rounding {beyond} > {tol}"
+    assert beyond_amb <= tol, f"near-tie error beyond rounding {beyond_amb} > {tol}"
     # routing tables of the layer are the stable sort of its own ids
     counts, offsets, ss, sp = (U.np_of(t[n]) for n in ("counts", "offsets", "sorted_slot", "slot_pos"))
     flat = idx_gpu.reshape(-1)
