@@ -1153,7 +1153,7 @@ def _random_config(seed: int, prefill: bool = False) -> MoEConfig:
                      shared_inter=int(r.choice([0, 0, 64, 256])), dtype=dtype, seed=seed)
 
 
-@pytest.mark.parametrize("seed", range(60))
+@pytest.mark.parametrize("seed", range(100))
 def test_layer_random_shapes(seed):
     """Seeded random layer shapes against the oracle (any_shape checks, see
     _check_layer): one stream; two streams where there is a shared expert;
@@ -1174,7 +1174,7 @@ def test_layer_random_shapes(seed):
         _check_layer(cfg, inp, lay, tuning=TU.to_struct(TU.limits(decode_tile_rows=32)), any_shape=True)
 
 
-@pytest.mark.parametrize("seed", range(8))
+@pytest.mark.parametrize("seed", range(16))
 def test_layer_random_prefill_shapes(seed):
     """Seeded random shapes at prefill sizes (1024 to 2048 tokens) against
     the oracle, one stream and, with a shared expert, two."""
