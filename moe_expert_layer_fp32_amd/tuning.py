@@ -67,7 +67,7 @@ def candidates_for(desc: L.MoeDesc, streams: int) -> list[dict]:
         for c in shared:            # 32-row tiles for the routed experts
             out.append(limits(c[0], c[1], decode_tile_rows=32))
         return out
-    shared = ((0, 0), (128, 128), (192, 192)) if (has_shared and streams == 2) else ((0, 0),)
+    shared = ((0, 0), (128, 128), (128, 0), (192, 192)) if (has_shared and streams == 2) else ((0, 0),)
     routed = ((0, 0), (160, 0)) if streams == 2 else ((0, 0),)
     for big in (0, NO_BIG):
         for sc in shared:
