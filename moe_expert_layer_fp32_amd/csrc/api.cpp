@@ -177,6 +177,9 @@ bool routed_tiled(const moe_desc* d, int N, int K) {
 // several workgroups per tile, up to SPLIT_WGS workgroups in all; the partial
 // sums are added in split order by the reduce pass. 1 = no split.
 constexpr int SPLIT_WGS = 512;
+// A split of exactly this many slices on 32-row bf16 tiles runs inside one
+// workgroup, one slice per wavefront (LdsArgs::wave_split).
+constexpr int WAVE_SPLIT = 4;
 int routed_splits(const moe_desc* d, int N, int K) {
   if (d->T >= PREFILL_T || !routed_tiled(d, N, K)) return 1;
   const long wgs = long(d->n_ffn) * ceil_div(N, 128);
@@ -415,6 +418,17 @@ moe_status run_routed(GemmArgs g, const moe_desc* d, GemmElem el, int planes, Ge
     L.min_rows = 1;
     L.max_rows = INT32_MAX;
     g.tiles_y = ceil_div(r_max(d), L.tile_rows) + g.n_groups;
+    if (splits == WAVE_SPLIT && L.tile_rows == 32 && el == ELEM_BF16 && planes <= 2 &&
+        (g.K / lds_chunk_elems(el)) % WAVE_SPLIT == 0) {
+      // The same four reduction ranges, one per wavefront of a workgroup that
+      // owns 32 features, added inside it in range order: the sums of the
+      // split-K reduce pass, bit for bit, without its launch or the partial
+      // sums' round trip through memory.
+      L.splits = 1;
+      L.wave_split = WAVE_SPLIT;
+      L.partial = nullptr;
+      L.max_wgs = capped_wgs(cap, 1);
+    }
     HIP_TRY(launch_gemm_lds(g, L, el, planes, epi, s, ev));
     return MOE_OK;
   }

@@ -87,9 +87,10 @@ struct M32F32 {
 constexpr int CH_BYTES = 256;              // bytes of one row per LDS chunk
 constexpr int LDS_ROW = CH_BYTES + 16;     // padded row stride (4-bank shift per row)
 
-template <class Tr, int S, int EPI, int NF, int BM, int RA, bool W_NT>
-__device__ __forceinline__ void gemm_lds_tile(const GemmArgs& a, const LdsArgs& L, uint8_t (&lds)[2][BM * LDS_ROW],
-                                              int g, int row0, int nrows, int out0, int nblock, int split) {
+template <class Tr, int S, int EPI, int NF, int BM, int RA, bool W_NT, int KW>
+__device__ __forceinline__ void gemm_lds_tile(const GemmArgs& a, const LdsArgs& L,
+                                              uint8_t (&lds)[2][KW * BM * LDS_ROW], int g, int row0, int nrows,
+                                              int out0, int nblock, int split) {
   constexpr int FT = NF / 32;                  // 32-feature tiles per wavefront
   constexpr int MBK = BM / 32;                 // 32-row blocks per tile
   constexpr int FB = FRAG_LANES * Tr::BPL;     // packed fragment bytes
@@ -102,17 +103,23 @@ __device__ __forceinline__ void gemm_lds_tile(const GemmArgs& a, const LdsArgs& 
   using acc_t = typename Tr::acc_t;
   const int lane = threadIdx.x & (WAVE - 1);
   const int wave = threadIdx.x / WAVE;
+  // KW > 1: the wavefronts split the reduction instead of the features (KW
+  // equal ranges of chunks, one per wavefront, all on the same WN * NF
+  // features); their sums are added at the end in range order, as the
+  // split-K reduce pass adds slices, so no partial sums leave the workgroup.
+  constexpr int WN = WG_WAVES / KW;
+  const int wave_n = wave % WN, wave_k = wave / WN;
 
   const int KT = a.K / Tr::KF;
   const int KC = a.K / CH_ELEMS;               // chunks in the whole reduction
-  const int c_begin = split * KC / L.splits;
-  const int c_end = (split + 1) * KC / L.splits;
-  const int nch = c_end - c_begin;
+  const int c_base = split * KC / L.splits;    // this slice's chunks (KW ranges of nch)
+  const int nch = ((split + 1) * KC / L.splits - c_base) / KW;
+  const int c_begin = c_base + wave_k * nch;   // this wavefront's range
 
   // ---- A: this wavefront's feature tiles, straight from global ----
   // A wavefront past the last feature tile (N not a multiple of the block)
   // computes a copy of the last tile and stores nothing.
-  const int ft_first = (nblock * WG_WAVES + wave) * FT;
+  const int ft_first = (nblock * WN + wave_n) * FT;
   const bool wave_live = ft_first * 32 < a.N;
   const int ft0 = wave_live ? ft_first : a.N / 32 - FT;
   const int r32 = lane & 31, half = lane >> 5;
@@ -196,7 +203,7 @@ __device__ __forceinline__ void gemm_lds_tile(const GemmArgs& a, const LdsArgs& 
     const int lin = threadIdx.x + i * WG_THREADS;
     const int r = lin / (CH_BYTES / 16);
     const int col = (lin % (CH_BYTES / 16)) * 16;
-    bsrc[i] = a.B + size_t(brow[i]) * a.ldb + size_t(c_begin) * CH_BYTES + col;
+    bsrc[i] = a.B + size_t(brow[i]) * a.ldb + size_t(c_base) * CH_BYTES + col;
     bdst[i] = r * LDS_ROW + col;
     bsv[i] = 1.f;
   }
@@ -212,15 +219,22 @@ __device__ __forceinline__ void gemm_lds_tile(const GemmArgs& a, const LdsArgs& 
   float ep_bs[MBK];   // activation scale of epilogue row m * 32 + r32
 #pragma unroll
   for (int m = 0; m < MBK; ++m) ep_bs[m] = 1.f;
-  // Two register stages of chunk loads (parity of the chunk index).
-  u32x4 bstage[2][LOADS];
+  // Two register stages of chunk loads (parity of the chunk index); with
+  // KW ranges, chunk c of every range (range q in LDS rows q * BM ...).
+  u32x4 bstage[2][KW][LOADS];
   auto load_b = [&](int st, int c) {
 #pragma unroll
-    for (int i = 0; i < LOADS; ++i) bstage[st][i] = *reinterpret_cast<const u32x4*>(bsrc[i] + size_t(c) * CH_BYTES);
+    for (int q = 0; q < KW; ++q)
+#pragma unroll
+      for (int i = 0; i < LOADS; ++i)
+        bstage[st][q][i] = *reinterpret_cast<const u32x4*>(bsrc[i] + size_t(q * nch + c) * CH_BYTES);
   };
   auto store_b = [&](int st, int buf) {
 #pragma unroll
-    for (int i = 0; i < LOADS; ++i) *reinterpret_cast<u32x4*>(&lds[buf][bdst[i]]) = bstage[st][i];
+    for (int q = 0; q < KW; ++q)
+#pragma unroll
+      for (int i = 0; i < LOADS; ++i)
+        *reinterpret_cast<u32x4*>(&lds[buf][q * BM * LDS_ROW + bdst[i]]) = bstage[st][q][i];
   };
 
   acc_t acc[NACC][FT][MBK];
@@ -239,7 +253,7 @@ __device__ __forceinline__ void gemm_lds_tile(const GemmArgs& a, const LdsArgs& 
   auto read_b = [&](op_t (&dst)[MBK], int buf, int ks) {
 #pragma unroll
     for (int m = 0; m < MBK; ++m)
-      dst[m] = Tr::load(&lds[buf][(m * 32 + r32) * LDS_ROW + ks * (Tr::KM * Tr::ESZ) + half * Tr::BPL]);
+      dst[m] = Tr::load(&lds[buf][(wave_k * BM + m * 32 + r32) * LDS_ROW + ks * (Tr::KM * Tr::ESZ) + half * Tr::BPL]);
   };
   // One chunk. Inside a step: read the next step's LDS operands, run this
   // step's matrix-core work, refill this step's weight slot RA steps ahead;
@@ -302,6 +316,40 @@ __device__ __forceinline__ void gemm_lds_tile(const GemmArgs& a, const LdsArgs& 
       chunk(std::integral_constant<int, 0>{}, c + 1);
     }
     if (c < nch) chunk(std::integral_constant<int, 1>{}, c);
+  }
+  if constexpr (KW > 1) {
+    // The ranges' sums meet in LDS buffer 1 (free: every read of the chunks
+    // came before the last chunk's barrier, and the next tile writes buffer
+    // 1 only after its first barrier, which range 0's wavefronts reach once
+    // done here); they add the others in range order and run the epilogue.
+    using part_t = typename Tr::part_t;
+    constexpr int PER = NACC * FT * MBK * 16;   // accumulator elements per lane
+    static_assert((KW - 1) * PER * WAVE * WN * sizeof(part_t) <= sizeof(lds[1]), "range sums must fit the LDS");
+    part_t* red = reinterpret_cast<part_t*>(&lds[1][0]);
+    auto at = [&](int q, int s, int f, int m, int j) {
+      return red + (((size_t(q - 1) * WN + wave_n) * PER + ((s * FT + f) * MBK + m) * 16 + j) * WAVE + lane);
+    };
+    if (wave_k > 0) {
+#pragma unroll
+      for (int s = 0; s < NACC; ++s)
+#pragma unroll
+        for (int f = 0; f < FT; ++f)
+#pragma unroll
+          for (int m = 0; m < MBK; ++m)
+#pragma unroll
+            for (int j = 0; j < 16; ++j) *at(wave_k, s, f, m, j) = acc[s][f][m][j];
+    }
+    __syncthreads();
+    if (wave_k > 0) return;
+    for (int q = 1; q < KW; ++q)
+#pragma unroll
+      for (int s = 0; s < NACC; ++s)
+#pragma unroll
+        for (int f = 0; f < FT; ++f)
+#pragma unroll
+          for (int m = 0; m < MBK; ++m)
+#pragma unroll
+            for (int j = 0; j < 16; ++j) acc[s][f][m][j] += *at(q, s, f, m, j);
   }
   if (!wave_live) return;
 
@@ -387,14 +435,14 @@ constexpr int ring_steps() { return S == 1 || BM == 128 || BM == 32 ? 8 : MOE_RI
 template <class Tr, int S, int EPI, int NF, int BM>
 constexpr int lds_waves_per_eu() { return BM <= 64 && NF == 32 && ring_steps<Tr, S, EPI, NF, BM>() <= 8 ? 2 : 1; }
 
-template <class Tr, int S, int EPI, int NF, int BM>
+template <class Tr, int S, int EPI, int NF, int BM, int KW>
 __global__ __launch_bounds__(WG_THREADS) __attribute__((amdgpu_waves_per_eu(lds_waves_per_eu<Tr, S, EPI, NF, BM>())))
 void gemm_lds_kernel(GemmArgs a, LdsArgs L) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds[2][BM * LDS_ROW];
+  __shared__ __attribute__((aligned(16))) uint8_t lds[2][KW * BM * LDS_ROW];
   __shared__ int offs[TILE_MAX_GROUPS + 1];
   stage_offsets(a, offs);
   const int tiles = count_tiles_lds(a, offs, BM, L.min_rows, L.max_rows);
-  const int nblocks = ceil_div(a.N, WG_WAVES * NF);
+  const int nblocks = ceil_div(a.N, (WG_WAVES / KW) * NF);
   const int total = tiles * nblocks;
   const int nwg = gridDim.x;
   const int xcd = blockIdx.x % 8, slot = blockIdx.x / 8, per_xcd_wg = nwg / 8;
@@ -428,9 +476,9 @@ void gemm_lds_kernel(GemmArgs a, LdsArgs L) {
     const bool once = a.offsets ? offs[g + 1] - offs[g] <= BM : a.dense_rows <= BM;
     constexpr int RA = ring_steps<Tr, S, EPI, NF, BM>();
     if (once)
-      gemm_lds_tile<Tr, S, EPI, NF, BM, RA, true>(a, L, lds, g, row0, nrows, out0, nblock, blockIdx.z);
+      gemm_lds_tile<Tr, S, EPI, NF, BM, RA, true, KW>(a, L, lds, g, row0, nrows, out0, nblock, blockIdx.z);
     else
-      gemm_lds_tile<Tr, S, EPI, NF, BM, RA, false>(a, L, lds, g, row0, nrows, out0, nblock, blockIdx.z);
+      gemm_lds_tile<Tr, S, EPI, NF, BM, RA, false, KW>(a, L, lds, g, row0, nrows, out0, nblock, blockIdx.z);
   }
 }
 
@@ -535,14 +583,14 @@ hipError_t launch_gemm_reduce(const GemmArgs& a, const LdsArgs& L, GemmElem elem
 
 int lds_chunk_elems(GemmElem elem) { return CH_BYTES / (elem == ELEM_F32 ? 4 : (elem == ELEM_BF16 ? 2 : 1)); }
 
-template <class Tr, int S, int EPI, int NF, int BM>
+template <class Tr, int S, int EPI, int NF, int BM, int KW = 1>
 static hipError_t launch_lds_one(const GemmArgs& a, const LdsArgs& L, hipStream_t stream, KernelEvents ev) {
   // persistent grid: at most `tiles_y` m-tiles per column block exist
-  const long bound = long(ceil_div(a.N, WG_WAVES * NF)) * a.tiles_y;
+  const long bound = long(ceil_div(a.N, (WG_WAVES / KW) * NF)) * a.tiles_y;
   const int nwg = int(std::max(8L, std::min(bound, long(L.max_wgs)) / 8 * 8));
   const dim3 grid(nwg, 1, L.splits);
   const bool reduce = L.splits > 1 && !L.fold_reduce;
-  hipError_t e = launch_timed((gemm_lds_kernel<Tr, S, EPI, NF, BM>), grid, dim3(WG_THREADS), stream, ev.start,
+  hipError_t e = launch_timed((gemm_lds_kernel<Tr, S, EPI, NF, BM, KW>), grid, dim3(WG_THREADS), stream, ev.start,
                               reduce ? nullptr : ev.stop, a, L);
   if (e != hipSuccess || !reduce) return e;
   return launch_gemm_reduce(a, L, std::is_same<typename Tr::part_t, int>::value ? ELEM_I8 : ELEM_BF16, GemmEpi(EPI),
@@ -558,6 +606,15 @@ static hipError_t launch_lds_shape(const GemmArgs& a, const LdsArgs& L, hipStrea
     if (L.wave_features == 64)
       return L.tile_rows == 64 ? launch_lds_one<Tr, S, EPI, 64, 64>(a, L, stream, ev)
                                : launch_lds_one<Tr, S, EPI, 64, 128>(a, L, stream, ev);
+  }
+  if (L.wave_split > 1) {
+    // the reduction split over the 4 wavefronts: 32-row tiles, bf16, one or
+    // two planes, no grid split, whole ranges of 256-byte chunks (the int8
+    // two-plane tile would spill: 104 bytes per lane)
+    if constexpr (S <= 2 && std::is_same<Tr, M32BF16>::value)
+      if (L.wave_split == WG_WAVES && L.tile_rows == 32 && L.splits == 1 && (a.K / (CH_BYTES / Tr::ESZ)) % WG_WAVES == 0)
+        return launch_lds_one<Tr, S, EPI, 32, 32, WG_WAVES>(a, L, stream, ev);
+    return hipErrorInvalidValue;
   }
   if (L.tile_rows == 32) return launch_lds_one<Tr, S, EPI, 32, 32>(a, L, stream, ev);
   return L.tile_rows == 64 ? launch_lds_one<Tr, S, EPI, 32, 64>(a, L, stream, ev)

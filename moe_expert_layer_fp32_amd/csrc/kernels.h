@@ -90,6 +90,10 @@ struct LdsArgs {
                        // the partial sums in split order (router -> gate)
   int group_m;         // tile order: <= 1 m-tile fastest; else panels of
                        // group_m m-tiles, column block next inside a panel
+  int wave_split;      // 0 or 1: the wavefronts of a workgroup own 4 * NF
+                       // features; 4: they split the reduction of NF features
+                       // into 4 ranges, added in range order inside the
+                       // workgroup (32-row tiles, splits == 1, bf16)
 };
 hipError_t launch_gemm_lds(const GemmArgs& a, const LdsArgs& L, GemmElem elem, int planes, GemmEpi epi,
                            hipStream_t stream, KernelEvents ev = {});

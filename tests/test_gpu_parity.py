@@ -1089,8 +1089,8 @@ def test_layer_decode_stream_theta(name, theta):
                                         ("dsv3_decode_share_bf16", {"shared_ffn1_wgs": 128})])
 def test_layer_decode_tile_rows_32(name, extra):
     """Decode workloads on 32-row routed tiles (moe_tuning.decode_tile_rows):
-    experts of at most 32 rows (DeepSeek-style share, split reduction) take
-    one tile, larger ones several (LongCat-style, W8A8 with its int8 path,
+    experts of at most 32 rows (DeepSeek-style share, reduction split over
+    the wavefronts of one workgroup) take one tile, larger ones several (LongCat-style, W8A8 with its int8 path,
     fp32); also beside a caller's theta and under a shared cap. Against the
     oracle, and equal to the 64-row call up to fp32 summation order."""
     L, DeviceLayer, to_device = _L()
@@ -1106,6 +1106,33 @@ def test_layer_decode_tile_rows_32(name, extra):
     torch.cuda.synchronize()
     _, dev = U.output_errors(U.np_of(y), U.np_of(y0).astype(np.float64), cfg.dtype)
     U.record(test="layer_decode_tile_rows_32", cfg=name, extra=extra, err_vs_64_rows=dev)
+
+
+def test_layer_wave_split_equals_slices():
+    """DeepSeek-style decode share: the routed gate/up reduction of 7168 is cut
+    into four 1792-element ranges either way. On 64-row tiles the ranges run
+    on four workgroups and the reduce pass adds their partial sums in order;
+    on 32-row tiles (bf16) they run on the four wavefronts of one workgroup
+    and are added in LDS in the same order. The SwiGLU rows h and the layer
+    output must therefore be equal, value for value, and the 32-row call must
+    still match the oracle."""
+    L, DeviceLayer, to_device = _L()
+    from moe_expert_layer_fp32_amd import tuning as TU
+    name = "dsv3_decode_share_bf16"
+    cfg, inp = U.inputs(name)
+    lay = U.device_layer(name)
+    U.say(f"[gpu] layer {name} wave-split gate/up against four split workgroups")
+    y32, t32 = lay.layer_with_tables(tuning=TU.to_struct(TU.limits(decode_tile_rows=32)), intermediates=True)
+    y64, t64 = lay.layer_with_tables(tuning=TU.to_struct(TU.limits(decode_tile_rows=64)), intermediates=True)
+    torch.cuda.synchronize()
+    assert torch.equal(t32["offsets"], t64["offsets"])
+    off = U.np_of(t32["offsets"])
+    rows = int(off[cfg.ffn_begin + cfg.n_ffn] - off[cfg.ffn_begin])
+    assert rows > 0
+    assert torch.equal(t32["h"][:rows].float(), t64["h"][:rows].float())
+    assert torch.equal(t32["rows"][:rows].float(), t64["rows"][:rows].float())
+    assert torch.equal(y32.float(), y64.float())
+    _check_layer(cfg, inp, lay, tuning=TU.to_struct(TU.limits(decode_tile_rows=32)))
 
 
 def _random_config(seed: int, prefill: bool = False) -> MoEConfig:
