@@ -1184,7 +1184,9 @@ def _random_config(seed: int, prefill: bool = False) -> MoEConfig:
 def test_layer_random_shapes(seed):
     """Seeded random layer shapes against the oracle (any_shape checks, see
     _check_layer): one stream; two streams where there is a shared expert;
-    every third seed also on 32-row decode tiles (moe_tuning)."""
+    every even seed also on 32-row decode tiles (moe_tuning; among them
+    bf16 shapes whose gate/up reduction is split four ways, which then runs on
+    the four wavefronts of one workgroup)."""
     L, DeviceLayer, to_device = _L()
     from moe_expert_layer_fp32_amd.layer import SecondStream
     from moe_expert_layer_fp32_amd import tuning as TU
@@ -1197,7 +1199,7 @@ def test_layer_random_shapes(seed):
     if cfg.shared_inter:
         y2 = _check_layer(cfg, inp, lay, second=SecondStream(), any_shape=True)
         assert torch.equal(_bits(y1), _bits(y2)), "two streams differ from one"
-    if seed % 3 == 0:
+    if seed % 2 == 0:
         _check_layer(cfg, inp, lay, tuning=TU.to_struct(TU.limits(decode_tile_rows=32)), any_shape=True)
 
 
