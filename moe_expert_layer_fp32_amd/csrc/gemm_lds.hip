@@ -20,7 +20,12 @@
 // (decode-sized shared expert), the reduction is cut into `splits` ranges;
 // each writes raw fp32 (int32 for int8) partial sums, and gemm_reduce_kernel
 // adds them in split order and applies the epilogue, so the result does not
-// depend on scheduling.
+// depend on scheduling. A four-way split of 32-row bf16 tiles can instead
+// run inside one workgroup (LdsArgs::wave_split): its four wavefronts own the
+// same 32 features and one range each, stage the four ranges' activation
+// chunks side by side in LDS, and add their sums in range order through LDS
+// before one epilogue - the same sums, with no partial sums in memory and no
+// reduce launch.
 #include <algorithm>
 #include <type_traits>
 
