@@ -1135,6 +1135,36 @@ def test_layer_wave_split_equals_slices():
     _check_layer(cfg, inp, lay, tuning=TU.to_struct(TU.limits(decode_tile_rows=32)))
 
 
+@pytest.mark.parametrize("T,lift", [(96, 2.0), (160, 3.0)])
+def test_layer_wave_split_multi_tile_experts(T, lift):
+    """A decode shape whose gate/up reduction is split four ways (8 resident
+    experts x 16 column blocks, d 1024: four 256-element ranges), with a logit
+    lift on the resident experts so that most of them get more than 32 rows:
+    on 32-row tiles they take two or more m-tiles (a ragged last one), each
+    reduced on the four wavefronts of one workgroup. Equal, value for value,
+    to the 64-row call (four split workgroups and the reduce pass) and
+    against the oracle."""
+    L, DeviceLayer, to_device = _L()
+    from moe_expert_layer_fp32_amd import tuning as TU
+    cfg = MoEConfig(name=f"wave_split_{T}", T=T, d=1024, E=32, k=4, gate="softmax", n_ffn=8, inter=2048,
+                    dtype="bf16", bias=("const", lift, 0, 8))
+    cfg.check()
+    inp = make_inputs(cfg, seed=23)
+    lay = DeviceLayer(cfg, inp)
+    U.say(f"[gpu] wave-split multi-tile experts T={T} lift={lift}")
+    y32, t32 = lay.layer_with_tables(tuning=TU.to_struct(TU.limits(decode_tile_rows=32)), intermediates=True)
+    y64, t64 = lay.layer_with_tables(tuning=TU.to_struct(TU.limits(decode_tile_rows=64)), intermediates=True)
+    torch.cuda.synchronize()
+    counts = U.np_of(t32["counts"])[:cfg.n_ffn]
+    assert (counts > 32).sum() >= 4, f"too few experts above one 32-row tile: {counts.tolist()}"
+    rows = int(counts.sum())
+    assert torch.equal(t32["offsets"], t64["offsets"])
+    assert torch.equal(t32["h"][:rows].float(), t64["h"][:rows].float())
+    assert torch.equal(y32.float(), y64.float())
+    _check_layer(cfg, inp, lay, tuning=TU.to_struct(TU.limits(decode_tile_rows=32)))
+    U.record(test="layer_wave_split_multi_tile_experts", T=T, counts=counts.tolist())
+
+
 def _random_config(seed: int, prefill: bool = False) -> MoEConfig:
     """A seeded layer shape drawn across the descriptor's ranges: the three
     compute types, both gates, plain / group-limited / per-group-quota
