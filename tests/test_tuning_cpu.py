@@ -98,3 +98,7 @@ def test_merge_into_and_shipped_table(TU, tmp_path):
     for key, entry in shipped.table.items():
         assert set(entry["limits"]) == set(TU.FIELDS), key
         assert all(int(v) >= 0 for v in entry["limits"].values()), key
+        # the kept limits are the fastest of the candidates timed for the entry
+        us = entry["us"]
+        assert TU.label(entry["limits"]) in us, key
+        assert us[TU.label(entry["limits"])] == min(us.values()), key
