@@ -1233,7 +1233,7 @@ def test_layer_random_shapes(seed):
         _check_layer(cfg, inp, lay, tuning=TU.to_struct(TU.limits(decode_tile_rows=32)), any_shape=True)
 
 
-@pytest.mark.parametrize("seed", range(16))
+@pytest.mark.parametrize("seed", range(32))
 def test_layer_random_prefill_shapes(seed):
     """Seeded random shapes at prefill sizes (1024 to 2048 tokens) against
     the oracle, one stream and, with a shared expert, two."""
